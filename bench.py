@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of the split prefix/suffix, tail-pad-skipping, non-causal
+attention forward (libjpa, gfx950) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2]
+
+One step = one jpa_forward call over the whole workload (all query rows of all
+heads, inputs already resident in HBM).  Prints ONE JSON line:
+
+* value / ms_per_step: valid-token TFLOP/s of the timed steps
+  (FLOPs = sum_b Hq * 4 * D * Nq_b * Nk_b, from jpa_plan);
+* roofline: the kernel's per-launch duration from HIP events recorded on the
+  stream it is launched on, against the bf16 dense MFMA peak;
+* cpu_baseline: the fp64 oracle timed on this host's cores;
+* parity: the GPU result of the timed call against that oracle run.
+
+Options for profiling runs: --no-cpu-baseline, --copy-probe BYTES (time a plain
+device copy of that many bytes; used to calibrate rocprofv3 HBM counters).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "split-KV attention fwd TFLOP/s (valid tokens) + % of MI355X bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X published dense bf16 MFMA peak
+KERNEL_NAME = "jpa_fwd_kernel"
+KERNEL_SOURCES = ("diffusion_transformer_joint_non_amd/csrc/jpa_kernel.hip",
+                  "diffusion_transformer_joint_non_amd/csrc/jpa_params.h")
+DEFAULT_WORKLOAD = 2
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return 1
+
+
+def cpu_baseline(w, x, flops_total):
+    """Time the oracle, as it stands, on the whole workload when that is small
+    enough (about half a minute of CPU work at most), else on a seeded subset of
+    query rows per head; report valid-token TFLOP/s scaled to what was run."""
+    import oracle
+    import synth
+    rows_total = int((~w.pad_query_mask()).sum())
+    est_row_s = 4.0e-9 * (w.prefix[0] + w.suffix_real[0]) * (1 + w.d / 64)
+    per_head = rows_total if est_row_s * rows_total * w.hq < 30.0 else max(
+        64, int(20.0 / (est_row_s * w.hq)))
+    t0 = time.perf_counter()
+    if per_head >= rows_total:
+        ref_o, ref_l = oracle.attention(*[x[n] for n in ("q", "k_prefix", "v_prefix", "k_suffix",
+                                                         "v_suffix", "cu_q", "cu_prefix",
+                                                         "cu_suffix_real")], x["scale"])
+        sample = f"full workload: {rows_total} real query rows x {w.hq} heads"
+        flops = flops_total
+        rows = None
+    else:
+        rows = synth.sample_query_rows(w, per_head)
+        ref_o, ref_l = oracle.attention_rows(*[x[n] for n in (
+            "q", "k_prefix", "v_prefix", "k_suffix", "v_suffix", "cu_q", "cu_prefix",
+            "cu_suffix_real")], x["scale"], rows)
+        segs = oracle.decode_segments(x["cu_q"], x["cu_prefix"], x["cu_suffix_real"])
+        starts = np.asarray([s.q_start for s in segs])
+        keys = np.asarray([s.keys for s in segs])
+        owner = np.searchsorted(starts, rows, side="right") - 1
+        flops = int(4 * w.d * keys[owner].sum())
+        sample = f"seeded subset: {rows.shape[1]} real query rows per head x {w.hq} heads"
+    dt = time.perf_counter() - t0
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+    return base, ref_o, ref_l, rows
+
+
+def copy_probe(nbytes: int, steps: int):
+    import torch
+    n = nbytes // 2
+    a = torch.empty(n, dtype=torch.int16, device="cuda").random_()
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_probe_bytes": n * 2, "read_bytes": n * 2, "write_bytes": n * 2,
+                      "ms": dt * 1e3, "GB/s": 2 * n * 2 / dt / 1e9}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(args.steps, 1))
+        return
+
+    import synth
+    from diffusion_transformer_joint_non_amd import jpa
+
+    w = synth.WORKLOADS[args.workload]
+    log(f"workload {w.wid} {w.name}: generating inputs")
+    x = synth.make_inputs(w)
+    dev = {n: torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(torch.bfloat16).cuda()
+           for n in ("q", "k_prefix", "v_prefix", "k_suffix", "v_suffix")}
+    rows, flops = jpa.jpa_plan(x["cu_q"], x["cu_prefix"], x["cu_suffix_real"], w.hq, w.d)
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty((w.hq, dev["q"].shape[0]), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        jpa.jpa_forward(dev["q"], dev["k_prefix"], dev["v_prefix"], dev["k_suffix"],
+                        dev["v_suffix"], x["cu_q"], x["cu_prefix"], x["cu_suffix_real"],
+                        x["scale"], out=out, lse=lse, stream=stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Per-launch events on the launch stream give the kernel's own duration;
+    # the synchronised wall clock around all K steps gives ms_per_step.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = np.asarray([e0.elapsed_time(e1) for e0, e1 in ev])
+    ms_per_step = wall * 1e3 / args.steps
+
+    kern_ms = float(np.mean(per_launch_ms))
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    traffic = load_traffic(w.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.hq, "heads_kv": w.hkv,
+                   "head_dim": w.d, "prefix": list(map(int, w.prefix)),
+                   "suffix_real": list(map(int, w.suffix_real)),
+                   "suffix_pad": list(map(int, w.suffix_pad)), "queries": w.queries,
+                   "valid_flops": flops},
+        "pct_of_bf16_peak": round(100.0 * flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": KERNEL_NAME,
+                     "kernel_ms": {"mean": round(kern_ms, 4),
+                                   "median": round(float(np.median(per_launch_ms)), 4),
+                                   "min": round(float(per_launch_ms.min()), 4),
+                                   "max": round(float(per_launch_ms.max()), 4)},
+                     "kernel_source_sha256_16": kernel_source_hash()},
+    }
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the fp64 oracle on the host")
+        base, ref_o, ref_l, sub = cpu_baseline(w, x, flops)
+        result["cpu_baseline"] = base
+        import oracle
+        go = out.float().cpu().numpy()
+        gl = lse.cpu().numpy()
+        if sub is None:
+            real = ~w.pad_query_mask()
+            err = oracle.compare(go[real], gl[:, real].T, ref_o[real], ref_l[:, real].T)
+        else:
+            err = oracle.compare(np.stack([go[sub[h], h] for h in range(w.hq)]),
+                                 np.stack([gl[h, sub[h]] for h in range(w.hq)]), ref_o, ref_l)
+        result["parity"] = {k: float(f"{v:.3e}") for k, v in err.items()}
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+// Host front end of libjpa: argument validation, segment decoding, launch
+// planning.  Everything here runs on the host and never reads device memory
+// (varlen metadata is host-side, so a call needs no device readback: vLLM-Omni
+// performance-patterns guide, section on removing per-layer syncs).
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "jpa.h"
+#include "jpa_params.h"
+
+namespace {
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+jpa_status check_offsets(const int32_t* cu, int32_t n) {
+    if (cu[0] != 0) return JPA_ERR_SEGMENTS;
+    for (int32_t i = 0; i + 1 < n; ++i)
+        if (cu[i + 1] < cu[i]) return JPA_ERR_SEGMENTS;
+    return JPA_OK;
+}
+
+// Decode row b (the pad of a row is segment 2b+1 of cu_suffix_real: sglang PR
+// #30107 review, implementation breakdown item 4).
+jpa_row_plan decode_row(int32_t b, const int32_t* cu_q, const int32_t* cu_prefix,
+                        const int32_t* cu_suffix_real) {
+    jpa_row_plan r;
+    r.q_start = cu_q[b];
+    r.q_slots = cu_q[b + 1] - cu_q[b];
+    r.prefix_start = cu_prefix[b];
+    r.prefix_len = cu_prefix[b + 1] - cu_prefix[b];
+    r.suffix_start = cu_suffix_real[2 * b];
+    r.suffix_real = cu_suffix_real[2 * b + 1] - cu_suffix_real[2 * b];
+    r.suffix_pad = cu_suffix_real[2 * b + 2] - cu_suffix_real[2 * b + 1];
+    r.q_real = r.q_slots - r.suffix_pad;
+    r.keys = r.prefix_len + r.suffix_real;
+    return r;
+}
+
+jpa_status check_segments(int32_t batch, const int32_t* cu_q, const int32_t* cu_prefix,
+                          const int32_t* cu_suffix_real) {
+    if (batch < 0) return JPA_ERR_VALUE;
+    if (!cu_q || !cu_prefix || !cu_suffix_real) return JPA_ERR_NULL;
+    jpa_status st;
+    if ((st = check_offsets(cu_q, batch + 1)) != JPA_OK) return st;
+    if ((st = check_offsets(cu_prefix, batch + 1)) != JPA_OK) return st;
+    if ((st = check_offsets(cu_suffix_real, 2 * batch + 1)) != JPA_OK) return st;
+    for (int32_t b = 0; b < batch; ++b) {
+        const jpa_row_plan r = decode_row(b, cu_q, cu_prefix, cu_suffix_real);
+        if (r.suffix_pad > r.q_slots) return JPA_ERR_SEGMENTS;
+        // int32 sum: both terms are differences of non-decreasing int32 offsets
+        if ((int64_t)r.prefix_len + r.suffix_real > INT32_MAX) return JPA_ERR_SEGMENTS;
+        if (r.q_real > 0 && (int64_t)r.prefix_len + r.suffix_real == 0) return JPA_ERR_SEGMENTS;
+    }
+    return JPA_OK;
+}
+
+jpa_status check_tensor(const jpa_tensor* t, int64_t tokens, int32_t heads, int32_t head_dim) {
+    if (!t) return JPA_ERR_NULL;
+    if (t->dtype != JPA_DTYPE_BF16) return JPA_ERR_DTYPE;
+    if (t->head_dim != head_dim || t->heads != heads || t->tokens != tokens) return JPA_ERR_SHAPE;
+    if (!t->data && t->tokens > 0) return JPA_ERR_NULL;
+    if (!aligned16(t->data)) return JPA_ERR_LAYOUT;
+    if (t->token_stride % 8 != 0 || t->head_stride % 8 != 0) return JPA_ERR_LAYOUT;
+    if (t->head_stride < t->head_dim) return JPA_ERR_LAYOUT;
+    if (t->token_stride < (int64_t)t->heads * t->head_stride) return JPA_ERR_LAYOUT;
+    return JPA_OK;
+}
+
+jpa_status validate(const jpa_tensor* q, const jpa_tensor* k_prefix, const jpa_tensor* v_prefix,
+                    const jpa_tensor* k_suffix, const jpa_tensor* v_suffix, int32_t batch,
+                    const int32_t* cu_q, const int32_t* cu_prefix, const int32_t* cu_suffix_real,
+                    float scale, const jpa_tensor* out, const float* lse) {
+    if (!q || !k_prefix || !v_prefix || !k_suffix || !v_suffix || !out) return JPA_ERR_NULL;
+    if (!std::isfinite(scale) || scale < 0.f) return JPA_ERR_VALUE;
+    jpa_status st = check_segments(batch, cu_q, cu_prefix, cu_suffix_real);
+    if (st != JPA_OK) return st;
+    const int32_t d = q->head_dim;
+    if (d != 64 && d != 128) return JPA_ERR_SHAPE;
+    const int32_t hq = q->heads, hkv = k_prefix->heads;
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return JPA_ERR_SHAPE;
+    const int64_t tq = cu_q[batch], tp = cu_prefix[batch], ts = cu_suffix_real[2 * batch];
+    if ((st = check_tensor(q, tq, hq, d)) != JPA_OK) return st;
+    if ((st = check_tensor(out, tq, hq, d)) != JPA_OK) return st;
+    if ((st = check_tensor(k_prefix, tp, hkv, d)) != JPA_OK) return st;
+    if ((st = check_tensor(v_prefix, tp, hkv, d)) != JPA_OK) return st;
+    if ((st = check_tensor(k_suffix, ts, hkv, d)) != JPA_OK) return st;
+    if ((st = check_tensor(v_suffix, ts, hkv, d)) != JPA_OK) return st;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JPA_ERR_LAYOUT;
+    return JPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+JPA_API jpa_status jpa_validate(const jpa_tensor* q, const jpa_tensor* k_prefix,
+                                const jpa_tensor* v_prefix, const jpa_tensor* k_suffix,
+                                const jpa_tensor* v_suffix, int32_t batch, const int32_t* cu_q,
+                                const int32_t* cu_prefix, const int32_t* cu_suffix_real,
+                                float scale, const jpa_tensor* out, const float* lse) {
+    return validate(q, k_prefix, v_prefix, k_suffix, v_suffix, batch, cu_q, cu_prefix,
+                    cu_suffix_real, scale, out, lse);
+}
+
+JPA_API jpa_status jpa_plan(int32_t batch, const int32_t* cu_q, const int32_t* cu_prefix,
+                            const int32_t* cu_suffix_real, int32_t heads_q, int32_t head_dim,
+                            jpa_row_plan* rows, int64_t* valid_flops) {
+    jpa_status st = check_segments(batch, cu_q, cu_prefix, cu_suffix_real);
+    if (st != JPA_OK) return st;
+    if (heads_q < 0 || head_dim < 0) return JPA_ERR_VALUE;
+    int64_t flops = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        const jpa_row_plan r = decode_row(b, cu_q, cu_prefix, cu_suffix_real);
+        if (rows) rows[b] = r;
+        flops += (int64_t)heads_q * 4 * head_dim * (int64_t)r.q_real * (int64_t)r.keys;
+    }
+    if (valid_flops) *valid_flops = flops;
+    return JPA_OK;
+}
+
+JPA_API jpa_status jpa_forward(const jpa_tensor* q, const jpa_tensor* k_prefix,
+                               const jpa_tensor* v_prefix, const jpa_tensor* k_suffix,
+                               const jpa_tensor* v_suffix, int32_t batch, const int32_t* cu_q,
+                               const int32_t* cu_prefix, const int32_t* cu_suffix_real,
+                               float scale, const jpa_tensor* out, float* lse, void* stream) {
+    jpa_status st = validate(q, k_prefix, v_prefix, k_suffix, v_suffix, batch, cu_q, cu_prefix,
+                             cu_suffix_real, scale, out, lse);
+    if (st != JPA_OK) return st;
+
+    jpa_kernel_params p;
+    std::memset(&p, 0, sizeof(p));
+    p.q = static_cast<const uint16_t*>(q->data);
+    p.kp = static_cast<const uint16_t*>(k_prefix->data);
+    p.vp = static_cast<const uint16_t*>(v_prefix->data);
+    p.ks = static_cast<const uint16_t*>(k_suffix->data);
+    p.vs = static_cast<const uint16_t*>(v_suffix->data);
+    p.out = static_cast<uint16_t*>(out->data);
+    p.lse = lse;
+    p.q_ts = q->token_stride;
+    p.kp_ts = k_prefix->token_stride;
+    p.vp_ts = v_prefix->token_stride;
+    p.ks_ts = k_suffix->token_stride;
+    p.vs_ts = v_suffix->token_stride;
+    p.o_ts = out->token_stride;
+    p.q_hs = q->head_stride;
+    p.kp_hs = k_prefix->head_stride;
+    p.vp_hs = v_prefix->head_stride;
+    p.ks_hs = k_suffix->head_stride;
+    p.vs_hs = v_suffix->head_stride;
+    p.o_hs = out->head_stride;
+    p.lse_ld = cu_q[batch];
+    p.hq = q->heads;
+    p.group = q->heads / k_prefix->heads;
+    p.c = scale * 1.4426950408889634f;
+
+    // One launch per JPA_MAX_ROWS batch rows; rows with no query slots are
+    // dropped from the plan.
+    int32_t b = 0;
+    while (b < batch) {
+        p.nrows = 0;
+        p.total_tiles = 0;
+        for (; b < batch && p.nrows < JPA_MAX_ROWS; ++b) {
+            const jpa_row_plan r = decode_row(b, cu_q, cu_prefix, cu_suffix_real);
+            if (r.q_slots == 0) continue;
+            jpa_kernel_row& kr = p.rows[p.nrows++];
+            kr.q_start = r.q_start;
+            kr.q_slots = r.q_slots;
+            kr.q_real = r.q_real;
+            kr.p_start = r.prefix_start;
+            kr.p_len = r.prefix_len;
+            kr.s_start = r.suffix_start;
+            kr.keys = r.keys;
+            kr.tile_start = p.total_tiles;
+            p.total_tiles += (r.q_slots + JPA_BLOCK_M - 1) / JPA_BLOCK_M;
+        }
+        if (p.nrows == 0) continue;
+        if ((int64_t)p.total_tiles * p.hq > INT32_MAX) return JPA_ERR_SHAPE;
+        if (jpa_launch_kernel(p, q->head_dim, stream) != 0) return JPA_ERR_HIP;
+    }
+    return JPA_OK;
+}
+
+JPA_API const char* jpa_status_str(jpa_status status) {
+    switch (status) {
+        case JPA_OK: return "JPA_OK";
+        case JPA_ERR_NULL: return "JPA_ERR_NULL: a required pointer is NULL";
+        case JPA_ERR_DTYPE: return "JPA_ERR_DTYPE: tensors must be bf16";
+        case JPA_ERR_SHAPE: return "JPA_ERR_SHAPE: inconsistent heads, head_dim or token extents";
+        case JPA_ERR_LAYOUT: return "JPA_ERR_LAYOUT: misaligned pointer or stride, or overlapping rows";
+        case JPA_ERR_SEGMENTS: return "JPA_ERR_SEGMENTS: invalid segment offsets";
+        case JPA_ERR_VALUE: return "JPA_ERR_VALUE: scale must be finite and >= 0, batch >= 0";
+        case JPA_ERR_HIP: return "JPA_ERR_HIP: the HIP runtime rejected the launch";
+    }
+    return "JPA_ERR_UNKNOWN";
+}
+
+JPA_API int32_t jpa_abi_version(void) { return JPA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+"""Thin ctypes binding over libjpa's C ABI (include/jpa.h), same names.
+
+Argument marshalling only: every step of the attention runs in the HIP
+library.  PyTorch supplies device memory and the current stream; nothing else
+is used from it.  If the library is not built this module raises on load --
+there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libjpa.so")
+
+JPA_OK = 0
+JPA_ERR_NULL = 1
+JPA_ERR_DTYPE = 2
+JPA_ERR_SHAPE = 3
+JPA_ERR_LAYOUT = 4
+JPA_ERR_SEGMENTS = 5
+JPA_ERR_VALUE = 6
+JPA_ERR_HIP = 7
+JPA_DTYPE_BF16 = 1
+BLOCK_M = 256          # query rows per workgroup (for launch accounting only)
+
+EXPORTED = ("jpa_forward", "jpa_validate", "jpa_plan", "jpa_status_str", "jpa_abi_version")
+
+
+class JpaTensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("tokens", ctypes.c_int64),
+        ("token_stride", ctypes.c_int64),
+        ("heads", ctypes.c_int32),
+        ("head_stride", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class JpaRowPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "q_start", "q_slots", "q_real", "prefix_start", "prefix_len",
+        "suffix_start", "suffix_real", "suffix_pad", "keys")]
+
+    def as_tuple(self):
+        return tuple(getattr(self, n) for n, _ in self._fields_)
+
+
+class JpaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class JpaArgumentError(JpaError, ValueError):
+    pass
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree libjpa.so (built by ``python -m
+    diffusion_transformer_joint_non_amd.build``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"libjpa.so not found at {_LIB_PATH}; build it with "
+            "`python -m diffusion_transformer_joint_non_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    tp = ctypes.POINTER(JpaTensor)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.jpa_forward.restype = ctypes.c_int
+    lib.jpa_forward.argtypes = [tp, tp, tp, tp, tp, ctypes.c_int32, i32p, i32p, i32p,
+                                ctypes.c_float, tp, ctypes.c_void_p, ctypes.c_void_p]
+    lib.jpa_validate.restype = ctypes.c_int
+    lib.jpa_validate.argtypes = [tp, tp, tp, tp, tp, ctypes.c_int32, i32p, i32p, i32p,
+                                 ctypes.c_float, tp, ctypes.c_void_p]
+    lib.jpa_plan.restype = ctypes.c_int
+    lib.jpa_plan.argtypes = [ctypes.c_int32, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
+                             ctypes.POINTER(JpaRowPlan), ctypes.POINTER(ctypes.c_int64)]
+    lib.jpa_status_str.restype = ctypes.c_char_p
+    lib.jpa_status_str.argtypes = [ctypes.c_int]
+    lib.jpa_abi_version.restype = ctypes.c_int32
+    lib.jpa_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def jpa_status_str(status: int) -> str:
+    return load_library().jpa_status_str(int(status)).decode()
+
+
+def jpa_abi_version() -> int:
+    return int(load_library().jpa_abi_version())
+
+
+def _raise_for(status: int):
+    if status == JPA_OK:
+        return
+    msg = jpa_status_str(status)
+    if status == JPA_ERR_HIP:
+        raise JpaError(status, msg)
+    raise JpaArgumentError(status, msg)
+
+
+def _i32(arr) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(arr, dtype=np.int64))
+    if a.size and (a.min() < -2**31 or a.max() >= 2**31):
+        raise ValueError("offsets must fit in int32")
+    return np.ascontiguousarray(a.astype(np.int32))
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def descriptor(t, data_ptr: Optional[int] = None) -> JpaTensor:
+    """jpa_tensor for a [tokens, heads, head_dim] bf16 torch tensor (or view)."""
+    import torch
+    if t.dim() != 3:
+        raise ValueError("expected a [tokens, heads, head_dim] tensor")
+    if t.stride(2) != 1 and t.shape[2] > 1:
+        raise ValueError("head_dim must be contiguous")
+    dtype = JPA_DTYPE_BF16 if t.dtype == torch.bfloat16 else 0
+    return JpaTensor(t.data_ptr() if data_ptr is None else data_ptr, t.shape[0], t.stride(0),
+                     t.shape[1], t.stride(1), t.shape[2], dtype)
+
+
+def jpa_plan(cu_q: Sequence[int], cu_prefix: Sequence[int], cu_suffix_real: Sequence[int],
+             heads_q: int, head_dim: int):
+    """Per-row bookkeeping (list of 9-tuples, see jpa_row_plan) and the int64
+    valid-token FLOP count, decoded by the C library on the host."""
+    lib = load_library()
+    cq, cp, cs = _i32(cu_q), _i32(cu_prefix), _i32(cu_suffix_real)
+    batch = max(cq.size - 1, 0)
+    if cp.size != batch + 1 or cs.size != 2 * batch + 1:
+        raise JpaArgumentError(JPA_ERR_SEGMENTS, "offset arrays must have B+1, B+1, 2B+1 entries")
+    rows = (JpaRowPlan * max(batch, 1))()
+    flops = ctypes.c_int64(0)
+    _raise_for(lib.jpa_plan(batch, _i32p(cq), _i32p(cp), _i32p(cs), int(heads_q), int(head_dim),
+                            rows, ctypes.byref(flops)))
+    return [rows[b].as_tuple() for b in range(batch)], int(flops.value)
+
+
+def _common(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix, cu_suffix_real):
+    cq, cp, cs = _i32(cu_q), _i32(cu_prefix), _i32(cu_suffix_real)
+    batch = max(cq.size - 1, 0)
+    if cp.size != batch + 1 or cs.size != 2 * batch + 1:
+        raise JpaArgumentError(JPA_ERR_SEGMENTS, "offset arrays must have B+1, B+1, 2B+1 entries")
+    descs = [descriptor(t) for t in (q, k_prefix, v_prefix, k_suffix, v_suffix)]
+    return cq, cp, cs, batch, descs
+
+
+def jpa_validate(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix, cu_suffix_real,
+                 scale: float, out, lse=None) -> int:
+    """Host-only check of a jpa_forward call; returns the jpa_status code."""
+    lib = load_library()
+    cq, cp, cs, batch, d = _common(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix,
+                                   cu_suffix_real)
+    od = descriptor(out)
+    return lib.jpa_validate(*[ctypes.byref(x) for x in d], batch, _i32p(cq), _i32p(cp), _i32p(cs),
+                            float(scale), ctypes.byref(od),
+                            None if lse is None else ctypes.c_void_p(lse.data_ptr()))
+
+
+def jpa_forward(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix, cu_suffix_real,
+                scale: float, out=None, lse=None, stream=None, with_lse: bool = True):
+    """Enqueue the attention on ``stream`` (default: torch's current stream).
+
+    q [Tq, Hq, D], k/v prefix [Tp, Hkv, D], k/v suffix [Ts, Hkv, D]: bf16 CUDA
+    (HIP) tensors or views with contiguous head_dim.  cu_* are host offsets
+    (lists, numpy arrays or CPU tensors).  Returns (out, lse); out/lse are
+    allocated here only when not given."""
+    import torch
+    lib = load_library()
+    cq, cp, cs, batch, d = _common(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix,
+                                   cu_suffix_real)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None and with_lse:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (q.shape[1], q.shape[0])):
+        raise JpaArgumentError(JPA_ERR_SHAPE, "lse must be contiguous fp32 [Hq, Tq]")
+    od = descriptor(out)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = lib.jpa_forward(*[ctypes.byref(x) for x in d], batch, _i32p(cq), _i32p(cp), _i32p(cs),
+                         float(scale), ctypes.byref(od),
+                         None if lse is None else ctypes.c_void_p(lse.data_ptr()),
+                         ctypes.c_void_p(handle))
+    _raise_for(st)
+    return out, lse

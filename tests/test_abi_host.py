@@ -1,0 +1,213 @@
+"""Host-side checks of the C ABI (no GPU needed; no kernel is run).
+
+* the in-tree libjpa.so loads and exports every function include/jpa.h declares;
+* jpa_plan's integers equal the hand-derived workload bookkeeping and the
+  oracle's decoding, bit for bit;
+* every validation error of jpa_validate is reachable from the host;
+* on a machine without a GPU, jpa_forward reports JPA_ERR_HIP instead of crashing.
+"""
+
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from diffusion_transformer_joint_non_amd import jpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jpa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"JPA_API\s+[\w\s\*]+?\b(jpa_\w+)\s*\(", text)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = jpa.load_library()
+    names = _declared_functions()
+    assert set(names) == set(jpa.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    m = re.search(r"#define JPA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert jpa.jpa_abi_version() == int(m.group(1))
+    for code in range(8):
+        s = jpa.jpa_status_str(code)
+        assert s.startswith("JPA_")
+    assert jpa.jpa_status_str(99) == "JPA_ERR_UNKNOWN"
+
+
+def test_plan_matches_golden_workloads():
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "segments.json")))["workloads"]
+    for wid, g in gold.items():
+        rows, flops = jpa.jpa_plan(g["cu_q"], g["cu_prefix"], g["cu_suffix_real"], g["hq"], g["d"])
+        assert [list(r) for r in rows] == g["rows"]
+        assert flops == g["valid_flops"]
+
+
+def _random_segments(rng, batch):
+    prefix = rng.integers(0, 300, batch)
+    real = rng.integers(0, 5000, batch)
+    pad = rng.integers(0, 200, batch)
+    both = rng.random(batch) < 0.5
+    prefix = np.where((real == 0) & (prefix == 0), 1, prefix)
+    lq = real + pad + np.where(both, prefix, 0)
+    cu_q = np.concatenate([[0], np.cumsum(lq)])
+    cu_p = np.concatenate([[0], np.cumsum(prefix)])
+    cs = [0]
+    for r, pd in zip(real, pad):
+        cs += [cs[-1] + r, cs[-1] + r + pd]
+    return cu_q, cu_p, np.asarray(cs)
+
+
+def test_plan_matches_oracle_decoding_random():
+    rng = np.random.default_rng(5)
+    for trial in range(200):
+        batch = int(rng.integers(0, 70))
+        cq, cp, cs = _random_segments(rng, batch)
+        hq, d = int(rng.choice([1, 8, 40])), int(rng.choice([64, 128]))
+        rows, flops = jpa.jpa_plan(cq, cp, cs, hq, d)
+        ref = oracle.decode_segments(cq, cp, cs)
+        assert [tuple(r) for r in rows] == [
+            (s.q_start, s.q_slots, s.q_real, s.p_start, s.p_len, s.s_start, s.s_real, s.s_pad, s.keys)
+            for s in ref]
+        assert flops == oracle.valid_flops(ref, hq, d)
+
+
+# ------------------------------------------------------------ validation paths
+
+def _valid_call(d=64, hq=4, hkv=2):
+    w = synth.custom_workload(hq, hkv, d, [3, 5], [7, 4], [2, 1], "prefix+suffix")
+    tq, tp, ts = w.tokens()
+    bf = torch.bfloat16
+    return dict(
+        q=torch.zeros(tq, hq, d, dtype=bf), k_prefix=torch.zeros(tp, hkv, d, dtype=bf),
+        v_prefix=torch.zeros(tp, hkv, d, dtype=bf), k_suffix=torch.zeros(ts, hkv, d, dtype=bf),
+        v_suffix=torch.zeros(ts, hkv, d, dtype=bf), cu_q=list(w.cu_q()),
+        cu_prefix=list(w.cu_prefix()), cu_suffix_real=list(w.cu_suffix_real()),
+        scale=d ** -0.5, out=torch.zeros(tq, hq, d, dtype=bf))
+
+
+def _validate(**kw):
+    return jpa.jpa_validate(**kw)
+
+
+def test_validate_accepts_valid_call():
+    assert _validate(**_valid_call()) == jpa.JPA_OK
+    assert _validate(**_valid_call(d=128, hq=6, hkv=6)) == jpa.JPA_OK
+    kw = _valid_call()
+    kw["lse"] = torch.zeros(4, kw["q"].shape[0])
+    assert _validate(**kw) == jpa.JPA_OK
+
+
+def test_validate_accepts_strided_views():
+    kw = _valid_call(d=128, hq=4, hkv=2)
+    fused = torch.zeros(kw["k_suffix"].shape[0], 4 + 2 * 2, 128, dtype=torch.bfloat16)
+    kw["k_suffix"] = fused[:, 4:6]
+    kw["v_suffix"] = fused[:, 6:8]           # token-strided slice of a fused QKV
+    assert _validate(**kw) == jpa.JPA_OK
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda kw: kw.update(q=kw["q"].half()), jpa.JPA_ERR_DTYPE),
+    (lambda kw: kw.update(k_suffix=kw["k_suffix"].float()), jpa.JPA_ERR_DTYPE),
+    (lambda kw: kw.update(q=torch.zeros(kw["q"].shape[0], 4, 96, dtype=torch.bfloat16)), jpa.JPA_ERR_SHAPE),
+    (lambda kw: kw.update(q=torch.zeros(kw["q"].shape[0], 3, 64, dtype=torch.bfloat16),
+                          out=torch.zeros(kw["q"].shape[0], 3, 64, dtype=torch.bfloat16)),
+     jpa.JPA_ERR_SHAPE),                                             # Hq % Hkv != 0
+    (lambda kw: kw.update(out=torch.zeros(kw["q"].shape[0], 2, 64, dtype=torch.bfloat16)),
+     jpa.JPA_ERR_SHAPE),                                             # out heads
+    (lambda kw: kw.update(v_prefix=kw["v_prefix"][:-1]), jpa.JPA_ERR_SHAPE),   # tokens vs cu
+    (lambda kw: kw.update(q=kw["q"][:-1], out=kw["out"][:-1]), jpa.JPA_ERR_SHAPE),
+    (lambda kw: kw.update(k_suffix=kw["k_suffix"][:, :1]), jpa.JPA_ERR_SHAPE),  # kv heads
+    (lambda kw: kw.update(out=torch.zeros(kw["q"].shape[0] * 4 * 64 + 4, dtype=torch.bfloat16)[4:]
+                          .view(kw["q"].shape[0], 4, 64)), jpa.JPA_ERR_LAYOUT),  # misaligned
+    (lambda kw: kw.update(k_prefix=torch.zeros(kw["k_prefix"].shape[0], 2, 68, dtype=torch.bfloat16)
+                          [:, :, :64].as_strided(kw["k_prefix"].shape, (132, 66, 1))),
+     jpa.JPA_ERR_LAYOUT),                                            # strides not multiples of 8
+    (lambda kw: kw.update(out=torch.zeros(kw["q"].shape[0] + 8, 64, dtype=torch.bfloat16)
+                          .as_strided(kw["q"].shape, (64, 8, 1))), jpa.JPA_ERR_LAYOUT),  # overlap
+    (lambda kw: kw.update(cu_q=[1] + kw["cu_q"][1:]), jpa.JPA_ERR_SEGMENTS),
+    (lambda kw: kw.update(cu_prefix=[0, 6, 5]), jpa.JPA_ERR_SEGMENTS),
+    (lambda kw: kw.update(cu_suffix_real=[0, 7, 6, 10, 12]), jpa.JPA_ERR_SEGMENTS),
+    (lambda kw: kw.update(scale=float("nan")), jpa.JPA_ERR_VALUE),
+    (lambda kw: kw.update(scale=-0.5), jpa.JPA_ERR_VALUE),
+    (lambda kw: kw.update(scale=float("inf")), jpa.JPA_ERR_VALUE),
+])
+def test_validate_rejects(mutate, code):
+    kw = _valid_call()
+    mutate(kw)
+    assert _validate(**kw) == code
+
+
+def test_validate_rejects_pad_longer_than_row_and_keyless_rows():
+    # pad 3 > 2 query slots
+    bf = torch.bfloat16
+    z = lambda n, h=2: torch.zeros(n, h, 64, dtype=bf)
+    assert jpa.jpa_validate(z(2), z(1), z(1), z(4), z(4), [0, 2], [0, 1], [0, 1, 4], 0.1, z(2)) \
+        == jpa.JPA_ERR_SEGMENTS
+    # real queries but no keys
+    assert jpa.jpa_validate(z(3), z(0), z(0), z(1), z(1), [0, 3], [0, 0], [0, 0, 1], 0.1, z(3)) \
+        == jpa.JPA_ERR_SEGMENTS
+    # an all-pad row with no keys is fine
+    assert jpa.jpa_validate(z(3), z(0), z(0), z(3), z(3), [0, 3], [0, 0], [0, 0, 3], 0.1, z(3)) \
+        == jpa.JPA_OK
+    # empty batch is fine
+    assert jpa.jpa_validate(z(0), z(0), z(0), z(0), z(0), [0], [0], [0], 0.1, z(0)) == jpa.JPA_OK
+
+
+def test_null_pointers_and_bad_counts_from_c():
+    lib = jpa.load_library()
+    kw = _valid_call()
+    d = [jpa.descriptor(kw[n]) for n in ("q", "k_prefix", "v_prefix", "k_suffix", "v_suffix")]
+    od = jpa.descriptor(kw["out"])
+    cq = np.asarray(kw["cu_q"], np.int32)
+    cp = np.asarray(kw["cu_prefix"], np.int32)
+    cs = np.asarray(kw["cu_suffix_real"], np.int32)
+    P = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    args = [ctypes.byref(x) for x in d]
+    assert lib.jpa_validate(*args, 2, P(cq), P(cp), P(cs), 0.1, ctypes.byref(od), None) == 0
+    assert lib.jpa_validate(None, *args[1:], 2, P(cq), P(cp), P(cs), 0.1, ctypes.byref(od), None) \
+        == jpa.JPA_ERR_NULL
+    assert lib.jpa_validate(*args, 2, None, P(cp), P(cs), 0.1, ctypes.byref(od), None) \
+        == jpa.JPA_ERR_NULL
+    assert lib.jpa_validate(*args, 2, P(cq), P(cp), P(cs), 0.1, None, None) == jpa.JPA_ERR_NULL
+    assert lib.jpa_validate(*args, -1, P(cq), P(cp), P(cs), 0.1, ctypes.byref(od), None) \
+        == jpa.JPA_ERR_VALUE
+    d0 = jpa.descriptor(kw["q"])
+    d0.data = None
+    assert lib.jpa_validate(ctypes.byref(d0), *args[1:], 2, P(cq), P(cp), P(cs), 0.1,
+                            ctypes.byref(od), None) == jpa.JPA_ERR_NULL
+    lse_bad = ctypes.c_void_p(np.zeros(200, np.float32).ctypes.data + 2)
+    assert lib.jpa_validate(*args, 2, P(cq), P(cp), P(cs), 0.1, ctypes.byref(od), lse_bad) \
+        == jpa.JPA_ERR_LAYOUT
+    # jpa_plan rejects what validation rejects and tolerates NULL outputs
+    assert lib.jpa_plan(2, P(cq), P(cp), P(cs), 4, 64, None, None) == 0
+    bad = np.asarray([0, 7, 6, 10, 12], np.int32)
+    assert lib.jpa_plan(2, P(cq), P(cp), P(bad), 4, 64, None, None) == jpa.JPA_ERR_SEGMENTS
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a GPU")
+def test_forward_without_gpu_reports_hip_error():
+    kw = _valid_call()
+    kw["out"] = torch.zeros_like(kw["q"])
+    with pytest.raises(jpa.JpaError) as e:
+        jpa.jpa_forward(**kw, lse=torch.zeros(4, kw["q"].shape[0]), stream=0)
+    assert e.value.status == jpa.JPA_ERR_HIP
+
+
+def test_forward_rejects_before_any_launch():
+    kw = _valid_call()
+    kw["scale"] = -1.0
+    with pytest.raises(jpa.JpaArgumentError) as e:
+        jpa.jpa_forward(**kw, lse=torch.zeros(4, kw["q"].shape[0]), stream=0)
+    assert e.value.status == jpa.JPA_ERR_VALUE

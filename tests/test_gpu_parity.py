@@ -1,0 +1,216 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Small and mid-size cases are compared element by element on every real query
+row; the two largest workloads on a seeded subset of 4096 query rows per head
+(every pad row is still checked in full).  Bar: max-abs 1e-2, mean-abs 1e-3,
+LSE abs 1e-3 in float32; pad rows exactly +0.0 and -inf; integer bookkeeping
+bit-exact.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from diffusion_transformer_joint_non_amd import jpa
+
+import gpu_harness as gh
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-test] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    jpa.load_library()
+
+
+# (hq, hkv, d, prefix, suffix_real, suffix_pad, queries): several tiles,
+# ragged tails on both phases, GQA, all-pad rows, empty rows.
+SMALL_CASES = [
+    (2, 2, 64, [8], [21], [3], "suffix"),
+    (4, 2, 128, [77], [300], [37], "prefix+suffix"),
+    (6, 3, 128, [0, 130], [513, 64], [0, 200], "suffix"),
+    (5, 1, 128, [256], [700], [5], "suffix"),
+    (3, 3, 64, [64, 1, 5], [64, 0, 1000], [64, 2, 0], "prefix+suffix"),
+    (2, 1, 128, [3, 0, 2], [0, 40, 0], [9, 0, 300], "suffix"),     # all-pad rows
+    (8, 8, 128, [511], [257], [255], "suffix"),
+    (2, 2, 64, [0, 0], [1, 2], [0, 1], "suffix"),                    # one key per row
+]
+
+
+@pytest.mark.parametrize("ci", range(len(SMALL_CASES)))
+def test_parity_small_cases(ci):
+    hq, hkv, d, p, r, pad, qm = SMALL_CASES[ci]
+    w = synth.custom_workload(hq, hkv, d, p, r, pad, qm, wid=500 + ci)
+    x = synth.make_inputs(w, pad_fill="garbage")
+    _say(f"small case {ci}: {SMALL_CASES[ci]}")
+    o, l = gh.run(x)
+    out, lse = gh.host(o, l)
+    err = gh.assert_parity_full(w, x, out, lse)
+    _say(f"small case {ci}: {err}")
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_parity_workload_full(wid):
+    w = synth.WORKLOADS[wid]
+    _say(f"workload {wid} ({w.name}): generating inputs")
+    x = synth.make_inputs(w)
+    o, l = gh.run(x)
+    out, lse = gh.host(o, l)
+    _say(f"workload {wid}: GPU done, running oracle")
+    err = gh.assert_parity_full(w, x, out, lse)
+    _say(f"workload {wid}: {err}")
+    rows, flops = jpa.jpa_plan(x["cu_q"], x["cu_prefix"], x["cu_suffix_real"], w.hq, w.d)
+    assert flops == oracle.valid_flops(oracle.decode_segments(
+        x["cu_q"], x["cu_prefix"], x["cu_suffix_real"]), w.hq, w.d)
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_parity_workload_sampled(wid):
+    from oracle_pool import oracle_rows_parallel
+    w = synth.WORKLOADS[wid]
+    _say(f"workload {wid} ({w.name}): generating inputs")
+    x = synth.make_inputs(w)
+    o, l = gh.run(x)
+    out, lse = gh.host(o, l)
+    del o, l
+    torch.cuda.empty_cache()
+    rows = synth.sample_query_rows(w, 4096)
+    _say(f"workload {wid}: GPU done, oracle on {rows.shape[1]} rows x {w.hq} heads")
+    ref_o, ref_l = oracle_rows_parallel(x, rows)
+    err = gh.assert_parity_rows(out, lse, rows, ref_o, ref_l)
+    gh.assert_pad_rows(w, out, lse)
+    assert np.isfinite(out).all() and np.isfinite(lse[:, ~w.pad_query_mask()]).all()
+    _say(f"workload {wid}: {err}")
+
+
+@pytest.mark.parametrize("case", [(1, None), (None, 1)])
+def test_pad_contents_are_never_read(case):
+    """Zero, N(0,100) and NaN pad slots (queries and K/V) give bitwise equal
+    outputs (sglang PR #30107 review: the pad is its own skipped segment)."""
+    if case[0] == 1:
+        w = synth.WORKLOADS[1]
+    else:
+        w = synth.custom_workload(4, 2, 128, [77, 3], [300, 129], [37, 64], "prefix+suffix", wid=600)
+    res = []
+    for fill in ("zero", "garbage", "nan"):
+        x = synth.make_inputs(w, pad_fill=fill)
+        o, l = gh.run(x)
+        res.append((gh.bits(o), l.cpu().numpy()))
+    for b in res[1:]:
+        assert np.array_equal(res[0][0], b[0])
+        assert np.array_equal(res[0][1].view(np.int32), b[1].view(np.int32))
+
+
+def test_split_equals_concat_bitwise():
+    """Same keys given as prefix+suffix or as one suffix: the key walk visits
+    the same tiles in the same order, so the result is bitwise identical
+    (sglang PR #26973 review: non-SP branches concatenate then attend)."""
+    w = synth.custom_workload(4, 4, 128, [77, 512], [819, 190], [2, 70], "prefix+suffix", wid=610)
+    x = synth.make_inputs(w, pad_fill="garbage")
+    o1, l1 = gh.run(x)
+    ks, vs, cs = [], [], [0]
+    p_off = s_off = 0
+    for b in range(w.batch):
+        P, R, pad = w.prefix[b], w.suffix_real[b], w.suffix_pad[b]
+        ks.append(np.concatenate([x["k_prefix"][p_off:p_off + P], x["k_suffix"][s_off:s_off + R + pad]]))
+        vs.append(np.concatenate([x["v_prefix"][p_off:p_off + P], x["v_suffix"][s_off:s_off + R + pad]]))
+        cs += [cs[-1] + P + R, cs[-1] + P + R + pad]
+        p_off += P
+        s_off += R + pad
+    x2 = dict(x)
+    x2.update(k_prefix=x["k_prefix"][:0], v_prefix=x["v_prefix"][:0], k_suffix=np.concatenate(ks),
+              v_suffix=np.concatenate(vs), cu_prefix=np.zeros(w.batch + 1, np.int32),
+              cu_suffix_real=np.asarray(cs, np.int32))
+    o2, l2 = gh.run(x2)
+    assert np.array_equal(gh.bits(o1), gh.bits(o2))
+    assert torch.equal(l1, l2)
+
+
+def test_strided_views_match_contiguous():
+    """Q/K/V as head slices of one fused QKV projection (token-strided views),
+    sglang PR #26973 review, Cosmos3 cross-attention snippet; vLLM-Omni guide:
+    test contiguous and row-strided layouts."""
+    hq, hkv, d = 8, 2, 128
+    w = synth.custom_workload(hq, hkv, d, [100], [600], [24], "suffix", wid=620)
+    x = synth.make_inputs(w)
+    o1, l1 = gh.run(x)
+    dev = gh.device_inputs(x)
+    ts = dev["k_suffix"].shape[0]
+    fused = torch.zeros(ts, hq + 2 * hkv, d, dtype=torch.bfloat16, device="cuda")
+    fused[:, :hq] = dev["q"]
+    fused[:, hq:hq + hkv] = dev["k_suffix"]
+    fused[:, hq + hkv:] = dev["v_suffix"]
+    dev2 = dict(dev, q=fused[:, :hq], k_suffix=fused[:, hq:hq + hkv], v_suffix=fused[:, hq + hkv:])
+    o2, l2 = gh.run(x, dev=dev2)
+    assert np.array_equal(gh.bits(o1), gh.bits(o2)) and torch.equal(l1, l2)
+    # strided output view too
+    big = torch.zeros(ts, hq, 2 * d, dtype=torch.bfloat16, device="cuda")
+    o3, _ = gh.run(x, dev=dev, out=big[:, :, :d])
+    assert np.array_equal(gh.bits(o1), gh.bits(o3))
+    assert torch.count_nonzero(big[:, :, d:]) == 0
+
+
+def test_deterministic_and_guard_bytes():
+    w = synth.custom_workload(6, 2, 128, [77], [1000], [13], "prefix+suffix", wid=630)
+    x = synth.make_inputs(w)
+    dev = gh.device_inputs(x)
+    tq = x["q"].shape[0]
+    guard = 4096
+    obuf = torch.full((tq * 6 * 128 + 2 * guard,), 12345, dtype=torch.int16, device="cuda")
+    lbuf = torch.full((6 * tq + 2 * guard,), 7.0, dtype=torch.float32, device="cuda")
+    out = obuf[guard:guard + tq * 6 * 128].view(torch.bfloat16).view(tq, 6, 128)
+    lse = lbuf[guard:guard + 6 * tq].view(6, tq)
+    o1, l1 = gh.run(x, dev=dev, out=out, lse=lse)
+    b1, lb1 = gh.bits(o1).copy(), l1.cpu().numpy().copy()
+    o2, l2 = gh.run(x, dev=dev)
+    assert np.array_equal(b1, gh.bits(o2)) and np.array_equal(lb1, l2.cpu().numpy())
+    assert torch.all(obuf[:guard] == 12345) and torch.all(obuf[-guard:] == 12345)
+    assert torch.all(lbuf[:guard] == 7.0) and torch.all(lbuf[-guard:] == 7.0)
+
+
+def test_without_lse_output():
+    w = synth.custom_workload(4, 4, 128, [33], [400], [7], "suffix", wid=640)
+    x = synth.make_inputs(w)
+    o1, _ = gh.run(x)
+    o2, l2 = gh.run(x, with_lse=False)
+    assert l2 is None and np.array_equal(gh.bits(o1), gh.bits(o2))
+
+
+def test_more_rows_than_one_launch():
+    """40 batch rows: the host splits them over two launches."""
+    rng = np.random.default_rng(3)
+    p = list(rng.integers(0, 100, 40))
+    r = list(rng.integers(1, 300, 40))
+    pad = list(rng.integers(0, 40, 40))
+    w = synth.custom_workload(2, 1, 64, p, r, pad, "prefix+suffix", wid=650)
+    x = synth.make_inputs(w, pad_fill="nan")
+    o, l = gh.run(x)
+    gh.assert_parity_full(w, x, *gh.host(o, l))
+
+
+def test_scale_zero_is_uniform_average():
+    w = synth.custom_workload(2, 2, 128, [70], [200], [6], "suffix", wid=660)
+    x = synth.make_inputs(w)
+    o, l = gh.run(x, scale=0.0)
+    gh.assert_parity_full(w, x, *gh.host(o, l), scale=0.0)
+
+
+def test_empty_batch_and_empty_rows():
+    w = synth.custom_workload(2, 2, 64, [5, 0], [0, 0], [0, 0], "suffix", wid=670)
+    x = synth.make_inputs(w)               # every row has zero query slots
+    o, l = gh.run(x)
+    assert o.shape[0] == 0
+    z = torch.zeros(0, 2, 64, dtype=torch.bfloat16, device="cuda")
+    out, lse = jpa.jpa_forward(z, z, z, z, z, [0], [0], [0], 0.125)
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0 and lse.shape == (2, 0)
