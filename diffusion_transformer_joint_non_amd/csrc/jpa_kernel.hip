@@ -327,9 +327,10 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
                             if (key0 + kb * 32 + key_of_reg[r0 + 1] >= Nk) e1 = 0.f;
                         }
                         pk[u] = pack_bf16(e0, e1);
-                        lsum = __builtin_amdgcn_fdot2_f32_bf16(
-                            __builtin_bit_cast(bf16x2_t, pk[u]),
-                            bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, lsum, false);
+                        // fp32 sum of the unrounded weights: the LSE must not
+                        // carry the bf16 rounding of P (it would reach 2^-9
+                        // relative on rows with few keys).
+                        lsum += e0 + e1;
                     }
                     pf[qb][kb][t] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
                 }
@@ -369,6 +370,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
                 w0[u] = pack_bf16(o[qb][db][2 * u] * inv, o[qb][db][2 * u + 1] * inv);
                 w1[u] = pack_bf16(o[qb][db][8 + 2 * u] * inv, o[qb][db][9 + 2 * u] * inv);
             }
+            if (!real) w0 = w1 = u32x4_t{0u, 0u, 0u, 0u};   // pad row: +0.0
             *reinterpret_cast<u32x4_t*>(dst + 32 * db) = w0;
             *reinterpret_cast<u32x4_t*>(dst + 32 * db + 8) = w1;
         }
