@@ -152,7 +152,10 @@ JPA_API jpa_status jpa_forward(const jpa_tensor* q, const jpa_tensor* k_prefix,
     p.lse_ld = cu_q[batch];
     p.hq = q->heads;
     p.group = q->heads / k_prefix->heads;
-    p.c = scale * 1.4426950408889634f;
+    // Softmax in base 2: the kernel scales scores by c = scale * log2(e).  c is
+    // kept >= 1e-30 so that masked scores (-FLT_MAX) still map to zero weight;
+    // below that the weights are uniform to fp32 precision anyway.
+    p.c = std::fmax(scale * 1.4426950408889634f, 1e-30f);
 
     // One launch per JPA_MAX_ROWS batch rows; rows with no query slots are
     // dropped from the plan.

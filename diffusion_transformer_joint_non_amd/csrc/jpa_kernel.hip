@@ -17,18 +17,21 @@
 // * The K rows feeding MFMA row i are permuted (bits 2 and 3 of i swapped) so
 //   that the accumulator registers of a lane, read eight at a time, are eight
 //   consecutive keys: they become the bf16 B operand of O^T += V^T P^T with
-//   no data movement.  The V^T rows feeding that product are permuted the
-//   same way so that each lane's accumulator holds 16 consecutive feature
-//   columns of one query, written with two 16-byte stores.
-// * K tiles sit in LDS as [key][d]; V tiles are transposed on the way in
-//   (register byte-permutes) to [d][key] so the PV operand is one 16-byte LDS
-//   read per lane.  Both use an XOR swizzle of 16-byte chunks so the eight
-//   lanes served together hit eight different bank groups.
+//   no data movement.
+// * K and V tiles are copied global -> LDS by direct-to-LDS loads (16 bytes
+//   per lane, no staging registers) into natural [key][d] tiles; the V^T
+//   operand is read with the gfx950 LDS transpose load ds_read_b64_tr_b16.
+//   XOR swizzles of the 16-byte (K) and 8-byte (V) chunks keep the reads free
+//   of bank conflicts.  K and V are triple-buffered; one barrier per tile.
+// * Software pipeline inside each wave over 32-key units: the QK^T MFMAs of
+//   unit u+1 are issued alongside the exponentials of unit u (second query
+//   block), and the PV MFMAs of unit u alongside the row max and the first
+//   query block's exponentials of unit u+1.
 // * The key loop walks one index space [0, P_b + R_b): a key below P_b is
 //   read from the prefix tensor, the rest from the suffix tensor, per row,
-//   so the two tensors are never concatenated and only the very last tile of
-//   the walk is partial.  Pad slots are never loaded; out-of-range rows are
-//   zero-filled in registers and their scores dropped.
+//   so the two tensors are never concatenated.  The tile grid is shifted so
+//   it ends exactly at P_b + R_b: only the first tile is partial (its head
+//   is masked) and no pad slot is ever loaded.
 // * Online softmax in the log2 domain, fp32, with a lazy rescale: the running
 //   reference max only moves when a tile's max exceeds it by more than 8
 //   (so P <= 2^8 and fp32 accumulators are safe), which skips the O rescale
@@ -40,6 +43,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "jpa_params.h"
 
 namespace {
@@ -49,6 +54,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -60,23 +67,16 @@ constexpr float kTau = 8.0f;                 // lazy-rescale threshold (log2 uni
 
 static_assert(kBM == JPA_BLOCK_M, "host and kernel tile height differ");
 
-// MFMA row i of the score product reads K row pi(i): bits 2 and 3 swapped.
+// MFMA row i of the score product reads K row pi(i): bits 2 and 3 swapped,
+// so that accumulator registers 8t..8t+7 of lane half h hold keys
+// 16t + 8h .. 16t + 8h + 7 -- exactly the B operand of the PV product.
 __device__ __forceinline__ int perm_k(int i) {
     return (i & 0x13) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
-// MFMA row i of the PV product reads V^T row sigma(i): i = b4 b3 b2 b1 b0 ->
-// b2 b4 b3 b1 b0, so accumulator register r of lane half h is column 16h + r.
-__device__ __forceinline__ int perm_v(int i) {
-    return (((i >> 2) & 1) << 4) | (((i >> 3) & 3) << 2) | (i & 3);
-}
-// Chunk swizzles (16-byte chunks).  For K rows read by lanes 0..15 of a half
-// (rows perm_k(0..15)) the swizzle is 0..15, distinct modulo 8 in each group
-// of 8 lanes; likewise for V^T rows perm_v(0..7) and perm_v(8..15).
+// 16-byte chunk swizzle of K rows: the rows perm_k(0..15) read by lanes 0..15
+// of a half get 0..15, distinct modulo 8 within each group of 8 lanes.
 __device__ __forceinline__ int swz_k(int row) {
     return (row & 3) | (((row >> 3) & 1) << 2) | (((row >> 2) & 1) << 3);
-}
-__device__ __forceinline__ int swz_v(int row) {
-    return (row & 3) | (((row >> 4) & 1) << 2);
 }
 
 __device__ __forceinline__ float other_half_max(float x) {
@@ -102,13 +102,13 @@ __global__ __launch_bounds__(kThreads, 1)
 void jpa_fwd_kernel(const jpa_kernel_params p) {
     constexpr int kDS = D / 16;              // 16-wide k-steps of QK^T
     constexpr int kDB = D / 32;              // 32-row blocks of O^T
-    constexpr int kCH = D / 8;               // 16-byte chunks per K row
-    constexpr int kRPP = kThreads / kCH;     // K rows loaded per pass
-    constexpr int kNP = kBN / kRPP;          // K load passes per tile
-    constexpr int kVCH = kBN / 8;            // 16-byte chunks per V^T row
+    constexpr int kCH = D / 8;               // 16-byte chunks per K/V row
+    constexpr int kTile = kBN * D;           // elements of one K or V tile
+    constexpr int kRowsPerOp = 512 / D;      // rows filled by one wave-wide 16 B/lane load
+    constexpr int kOpsPerWave = kBN / kRowsPerOp / kWaves;
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBN * D];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * kBN];
+    // Three K tiles then three V tiles, all [key][d] (96 KB at D = 128).
+    __shared__ __attribute__((aligned(16))) uint16_t lds[6 * kTile];
 
     // ---- work item: XCD-grouped order over (head, row, query tile)
     const int nblk = gridDim.x;
@@ -157,88 +157,80 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     // key k < P is prefix token p_row0 + k; key k >= P is suffix slot s_row0 + k
     const int64_t p_row0 = p.rows[b].p_start;
     const int64_t s_row0 = (int64_t)p.rows[b].s_start - P;
+    // The key walk is shifted so that the tiles end exactly at Nk: only tile
+    // 0 can be partial, and its missing keys are the negative indices.
+    const int ntiles = (Nk + kBN - 1) / kBN;
+    const int shift = ntiles * kBN - Nk;
 
     // ---- Q fragments (B operand of S^T = K Q^T): lane (j, h) holds
-    //      q[row j][16*ds + 8*h .. +7] for every k-step ds.
+    //      q[row j][16*ds + 8*h .. +7] for every k-step ds.  Rows past the
+    //      real queries re-read the last real row (never a pad slot); their
+    //      results are discarded.
     bf16x8_t qf[kQB][kDS];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-        const int qi = m0 + wave * (kQB * 32) + qb * 32 + j;
-        const bool ok = qi < q_real;
-        const uint16_t* src = p.q + (int64_t)(q_start + (ok ? qi : 0)) * p.q_ts + (int64_t)hq * p.q_hs + 8 * h;
+        const int qi = min(m0 + wave * (kQB * 32) + qb * 32 + j, q_real - 1);
+        const uint16_t* src = p.q + (int64_t)(q_start + qi) * p.q_ts + (int64_t)hq * p.q_hs + 8 * h;
 #pragma unroll
-        for (int ds = 0; ds < kDS; ++ds) {
-            u32x4_t v = ok ? load16(src + 16 * ds) : u32x4_t{0u, 0u, 0u, 0u};
-            qf[qb][ds] = __builtin_bit_cast(bf16x8_t, v);
-        }
+        for (int ds = 0; ds < kDS; ++ds) qf[qb][ds] = __builtin_bit_cast(bf16x8_t, load16(src + 16 * ds));
     }
+    // Register classes: Q fragments and the O accumulators live in AGPRs (only
+    // MFMAs touch them in the loop); scores live in VGPRs where the softmax
+    // VALU work reads them.  Empty asm statements pin the classes.
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int ds = 0; ds < kDS; ++ds) asm("" : "+a"(qf[qb][ds]));
 
-    // ---- global -> register tile loads
-    const int kc = tid % kCH, kr = tid / kCH;          // K: chunk, first row
-    const int vq = tid & 15, vdc = tid >> 4;           // V: key quad, d chunk
-    const bool v_active = vdc < kCH;
-    u32x4_t kreg[kNP];
-    u32x4_t vreg[4];
-
-    auto load_tile = [&](int key0) {
+    // ---- global -> LDS tile loads, 16 bytes per lane straight into LDS
+    //      (global_load_lds_dwordx4: lane l of a wave lands at base + 16*l).
+    //      A wave instruction fills kRowsPerOp consecutive key rows; each lane
+    //      fetches the global chunk that belongs at its physical LDS slot,
+    //      which realises the XOR swizzles.  Negative keys (the head of tile 0)
+    //      re-read key 0; their scores are masked.  No pad slot is touched.
+    auto load_tile = [&](int t) {
+        const int slot = t % 3;
+        uint16_t* kdst = lds + slot * kTile;
+        uint16_t* vdst = lds + (3 + slot) * kTile;
 #pragma unroll
-        for (int i = 0; i < kNP; ++i) {
-            const int key = key0 + kr + kRPP * i;
-            const uint16_t* row = key < P ? kp + (p_row0 + key) * p.kp_ts : ks + (s_row0 + key) * p.ks_ts;
-            kreg[i] = key < Nk ? load16(row + kc * 8) : u32x4_t{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = key0 + 4 * vq + r;
-            const uint16_t* row = key < P ? vp + (p_row0 + key) * p.vp_ts : vs + (s_row0 + key) * p.vs_ts;
-            vreg[r] = (v_active && key < Nk) ? load16(row + vdc * 8) : u32x4_t{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < kNP; ++i) {
-            const int row = kr + kRPP * i;
-            const int chunk = (kc ^ swz_k(row)) & (kCH - 1);
-            *reinterpret_cast<u32x4_t*>(k_lds + row * D + chunk * 8) = kreg[i];
-        }
-        if (v_active) {
-            // 4 keys x 8 features -> 8 feature rows of 4 keys (transpose).
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int w = e >> 1;
-                uint32_t lo, hi;
-                if (e & 1) {
-                    lo = (vreg[0][w] >> 16) | (vreg[1][w] & 0xFFFF0000u);
-                    hi = (vreg[2][w] >> 16) | (vreg[3][w] & 0xFFFF0000u);
-                } else {
-                    lo = (vreg[0][w] & 0xFFFFu) | (vreg[1][w] << 16);
-                    hi = (vreg[2][w] & 0xFFFFu) | (vreg[3][w] << 16);
-                }
-                const int row = vdc * 8 + e;
-                const int chunk = (vq >> 1) ^ swz_v(row);
-                *reinterpret_cast<u32x2_t*>(vt_lds + row * kBN + chunk * 8 + (vq & 1) * 4) =
-                    u32x2_t{lo, hi};
-            }
+        for (int i = 0; i < kOpsPerWave; ++i) {
+            const int row0 = (wave * kOpsPerWave + i) * kRowsPerOp;
+            const int row = row0 + lane / kCH;
+            const int pc = lane % kCH;
+            const int key = max(t * kBN - shift + row, 0);
+            const bool pre = key < P;
+            const uint16_t* gk = (pre ? kp + (p_row0 + key) * p.kp_ts : ks + (s_row0 + key) * p.ks_ts) +
+                                 ((pc ^ swz_k(row)) & (kCH - 1)) * 8;
+            const uint16_t* gv = (pre ? vp + (p_row0 + key) * p.vp_ts : vs + (s_row0 + key) * p.vs_ts) +
+                                 ((pc ^ (2 * (row & 3))) & (kCH - 1)) * 8;
+            __builtin_amdgcn_global_load_lds(gk, (__attribute__((address_space(3))) void*)(kdst + row0 * D),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gv, (__attribute__((address_space(3))) void*)(vdst + row0 * D),
+                                             16, 0, 0);
         }
     };
 
     // ---- per-lane LDS fragment addresses (loop invariant)
+    //  K (A operand of S^T = K Q^T): lane (j, h) reads row perm_k(j), 16-byte
+    //  chunk 2*ds + h of the [key][d] tile.
+    //  V (A operand of O^T = V^T P^T) comes from the [key][d] tile through
+    //  ds_read_b64_tr_b16: in each 16-lane group, source lane 4k+q points at
+    //  key row (.. + k), features 4q..4q+3 of the group's 16-feature block, and
+    //  result lane i receives feature i of those 4 keys.  Two such reads give
+    //  a lane the 8 consecutive keys 16t + 8h .. +7 of one feature column.
     const int krow = perm_k(j);
-    const int vrow = perm_v(j);
     int k_off[kDS];
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds)
         k_off[ds] = krow * D + (((2 * ds + h) ^ swz_k(krow)) & (kCH - 1)) * 8;
-    int v_off[kKB][2];
+    const int tr_k = (lane & 15) >> 2;       // key offset supplied by this lane
+    const int tr_q = lane & 3;               // 4-feature group supplied by this lane
+    const int tr_half = (lane >> 4) & 1;     // which 16 features of the 32-block
+    const int v_row = (8 * h + tr_k) * D;
+    int v_col[kDB];
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-            v_off[kb][t] = vrow * kBN + (((4 * kb + 2 * t + h) ^ swz_v(vrow)) & (kVCH - 1)) * 8;
-    // key offset (inside a 32-key block) of accumulator register r
-    int key_of_reg[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) key_of_reg[r] = perm_k(8 * (r >> 2) + 4 * h + (r & 3));
+    for (int db = 0; db < kDB; ++db)
+        v_col[db] = (((8 * db + 4 * tr_half + tr_q) ^ (4 * tr_k)) & (D / 4 - 1)) * 4;
 
     f32x16_t o[kQB][kDB];
     float m_ref[kQB], l_sum[kQB];
@@ -247,133 +239,184 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         m_ref[qb] = -INFINITY;
         l_sum[qb] = 0.f;
 #pragma unroll
-        for (int db = 0; db < kDB; ++db)
+        for (int db = 0; db < kDB; ++db) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
+            asm("" : "+a"(o[qb][db]));
+        }
     }
-
     const float c = p.c;
-    const int ntiles = (Nk + kBN - 1) / kBN;
-    load_tile(0);
 
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int key0 = kt * kBN;
-        __syncthreads();                     // previous tile fully consumed
-        store_tile();
-        __syncthreads();
-        if (kt + 1 < ntiles) load_tile(key0 + kBN);   // in flight during compute
-
-        // S^T = K Q^T
-        f32x16_t s[kQB][kKB];
+    // One "unit" = 32 keys of a tile (kb = 0 or 1).
+    // S^T = K Q^T for one unit, both query blocks (each K fragment feeds two MFMAs)
+    auto qk = [&](f32x16_t (&s)[kQB], int t, int kb) {
+        const uint16_t* base = lds + (t % 3) * kTile + kb * 32 * D;
 #pragma unroll
-        for (int kb = 0; kb < kKB; ++kb) {
+        for (int ds = 0; ds < kDS; ++ds) {
+            const bf16x8_t kf = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const u32x4_t*>(base + k_off[ds]));
 #pragma unroll
             for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
-#pragma unroll
-            for (int ds = 0; ds < kDS; ++ds) {
-                const bf16x8_t kf = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(k_lds + kb * 32 * D + k_off[ds]));
-#pragma unroll
-                for (int qb = 0; qb < kQB; ++qb)
-                    s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ds], s[qb][kb], 0, 0, 0);
-            }
+                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ds],
+                                                                ds == 0 ? f32x16_t{} : s[qb], 0, 0, 0);
         }
-
-        const bool partial = key0 + kBN > Nk;
-        bf16x8_t pf[kQB][kKB][2];
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-            if (partial) {
-#pragma unroll
-                for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (key0 + kb * 32 + key_of_reg[r] >= Nk) s[qb][kb][r] = -INFINITY;
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-            mx = other_half_max(mx);
-            const float mt = mx * c;
-            const float mo = m_ref[qb];
-            const bool need = mt > mo + kTau;
-            const float mn = need ? mt : mo;
-            if (__builtin_amdgcn_ballot_w64(need)) {
-                const float alpha = __builtin_amdgcn_exp2f(mo - mn);
-                l_sum[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < kDB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-            }
-            m_ref[qb] = mn;
-            float lsum = l_sum[qb];
-#pragma unroll
-            for (int kb = 0; kb < kKB; ++kb) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    uint32_t pk[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int r0 = 8 * t + 2 * u;
-                        float e0 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r0], c, -mn));
-                        float e1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r0 + 1], c, -mn));
-                        if (partial) {
-                            if (key0 + kb * 32 + key_of_reg[r0] >= Nk) e0 = 0.f;
-                            if (key0 + kb * 32 + key_of_reg[r0 + 1] >= Nk) e1 = 0.f;
-                        }
-                        pk[u] = pack_bf16(e0, e1);
-                        // fp32 sum of the unrounded weights: the LSE must not
-                        // carry the bf16 rounding of P (it would reach 2^-9
-                        // relative on rows with few keys).
-                        lsum += e0 + e1;
-                    }
-                    pf[qb][kb][t] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-                }
-            }
-            l_sum[qb] = lsum;
-        }
-
-        // O^T += V^T P^T
+        for (int qb = 0; qb < kQB; ++qb) asm("" : "+v"(s[qb]));
+    };
+    // O^T += V^T P^T for one unit (each V fragment feeds two MFMAs)
+    auto pv = [&](int t, int kb, const bf16x8_t (&p0)[2], const bf16x8_t (&p1)[2]) {
+        const uint16_t* base = lds + (3 + t % 3) * kTile + kb * 32 * D + v_row;
 #pragma unroll
         for (int db = 0; db < kDB; ++db)
 #pragma unroll
-            for (int kb = 0; kb < kKB; ++kb)
+            for (int u = 0; u < 2; ++u) {
+                const uint16_t* a = base + 16 * u * D + v_col[db];
+                const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4_t*)(a));
+                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4_t*)(a + 4 * D));
+                const bf16x8_t vf = __builtin_bit_cast(
+                    bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p0[u], o[0][db], 0, 0, 0);
+                o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p1[u], o[1][db], 0, 0, 0);
+            }
+    };
+    // Scores of negative keys (head of tile 0) -> -FLT_MAX.  A finite value
+    // keeps a fully masked unit NaN-free: its weights underflow to 0.
+    auto mask_head = [&](f32x16_t (&s)[kQB], int kb) {
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const bf16x8_t vf = __builtin_bit_cast(
-                        bf16x8_t, *reinterpret_cast<const u32x4_t*>(vt_lds + db * 32 * kBN + v_off[kb][t]));
+        for (int r = 0; r < 16; ++r) {
+            const bool dead = kb * 32 + perm_k(8 * (r >> 2) + 4 * h + (r & 3)) < shift;
 #pragma unroll
-                    for (int qb = 0; qb < kQB; ++qb)
-                        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][t], o[qb][db], 0, 0, 0);
-                }
+            for (int qb = 0; qb < kQB; ++qb) s[qb][r] = dead ? -3.402823466e38f : s[qb][r];
+        }
+    };
+    // Move the reference max of each query block when the unit's max exceeds
+    // it by more than kTau (log2 units); returns whether any lane moved.
+    auto update_ref = [&](const f32x16_t (&s)[kQB], float (&alpha)[kQB]) {
+        bool any = false;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            float mx = s[qb][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qb][r]);
+            const float mt = fmaxf(other_half_max(mx) * c, -1e30f);
+            const bool need = mt > m_ref[qb] + kTau;
+            const float mn = need ? mt : m_ref[qb];
+            alpha[qb] = __builtin_amdgcn_exp2f(m_ref[qb] - mn);
+            m_ref[qb] = mn;
+            any |= need;
+        }
+        return __builtin_amdgcn_ballot_w64(any) != 0;
+    };
+    auto rescale = [&](const float (&alpha)[kQB]) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            l_sum[qb] *= alpha[qb];
+#pragma unroll
+            for (int db = 0; db < kDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha[qb];
+        }
+    };
+    // P = 2^(S*c - m) for one query block of a unit, as two bf16 B-operand
+    // fragments (keys 16u + 8h .. +7); returns the fp32 sum of the weights
+    // (unrounded, so the LSE does not carry the bf16 rounding of P).
+    auto exp_pack = [&](const f32x16_t& s, float m, bf16x8_t (&pf)[2]) {
+        float lsum = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            uint32_t pk[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int r0 = 8 * u + 2 * w;
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(s[r0], c, -m));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(s[r0 + 1], c, -m));
+                pk[w] = pack_bf16(e0, e1);
+                lsum += e0 + e1;
+            }
+            pf[u] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+        }
+        return lsum;
+    };
+
+    // ---- prologue: tiles 0 and 1 into LDS; scores, reference max and the
+    //      first query block's weights of unit (0, 0).
+    f32x16_t sA[kQB], sB[kQB];
+    bf16x8_t pA0[2], pB0[2], p1[2];
+    load_tile(0);
+    if (ntiles > 1) load_tile(1);
+    __syncthreads();
+    qk(sA, 0, 0);
+    mask_head(sA, 0);
+    {
+        float alpha[kQB];
+        update_ref(sA, alpha);               // O and l are still zero
+        l_sum[0] = exp_pack(sA[0], m_ref[0], pA0);
     }
 
-    // ---- epilogue: normalise, bf16 round-to-nearest-even, pad rows as zeros
+    // ---- steady state, per tile t (two units):
+    //   unit (t,0)  X: QK of unit (t,1)    || weights of (t,0), query block 1
+    //               Y: PV of unit (t,0)    || max of (t,1), reference update,
+    //                                          weights of (t,1), query block 0
+    //   unit (t,1)  X: QK of unit (t+1,0)  || weights of (t,1), query block 1
+    //               Y: PV of unit (t,1)    || max of (t+1,0), reference update,
+    //                                          weights of (t+1,0), query block 0
+    //   Tile t+2 is fetched at the start, one barrier at the end.  On the last
+    //   tile the look-ahead re-reads unit (t,0) (already counted, so it can
+    //   never move the reference) and its weights are dropped.
+    auto body = [&](int t, auto first) {
+        if (t + 2 < ntiles) load_tile(t + 2);
+        float alpha[kQB];
+        // unit (t,0)
+        qk(sB, t, 1);
+        l_sum[1] += exp_pack(sA[1], m_ref[1], p1);
+        if constexpr (decltype(first)::value) mask_head(sB, 1);
+        pv(t, 0, pA0, p1);
+        {
+            const bool any = update_ref(sB, alpha);
+            float ts0 = exp_pack(sB[0], m_ref[0], pB0);
+            asm volatile("" : "+v"(ts0), "+v"(pB0[0]), "+v"(pB0[1]));   // computed here, not after the branch
+            if (any) rescale(alpha);
+            l_sum[0] += ts0;
+        }
+        // unit (t,1)
+        const bool last = t + 1 == ntiles;
+        qk(sA, last ? t : t + 1, 0);
+        l_sum[1] += exp_pack(sB[1], m_ref[1], p1);
+        pv(t, 1, pB0, p1);
+        {
+            const bool any = update_ref(sA, alpha);
+            float ts0 = exp_pack(sA[0], m_ref[0], pA0);
+            asm volatile("" : "+v"(ts0), "+v"(pA0[0]), "+v"(pA0[1]));
+            if (any) rescale(alpha);
+            l_sum[0] += last ? 0.f : ts0;
+        }
+        __syncthreads();
+    };
+    body(0, std::true_type{});
+    for (int t = 1; t < ntiles; ++t) body(t, std::false_type{});
+
+    // ---- epilogue: normalise, bf16 round-to-nearest-even, pad rows as zeros.
+    //      O^T accumulator register r of lane half h is feature
+    //      32*db + 8*(r/4) + 4*h + r%4.
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
         const int qi = m0 + wave * (kQB * 32) + qb * 32 + j;
         if (qi >= q_slots) continue;
         const bool real = qi < q_real;
         const float l_tot = other_half_sum(l_sum[qb]);
-        const float inv = real ? 1.0f / l_tot : 0.f;
-        uint16_t* dst = out_h + (int64_t)(q_start + qi) * p.o_ts + 16 * h;
+        const float inv = 1.0f / l_tot;
+        uint16_t* dst = out_h + (int64_t)(q_start + qi) * p.o_ts + 4 * h;
 #pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-            u32x4_t w0, w1;
+        for (int db = 0; db < kDB; ++db)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                w0[u] = pack_bf16(o[qb][db][2 * u] * inv, o[qb][db][2 * u + 1] * inv);
-                w1[u] = pack_bf16(o[qb][db][8 + 2 * u] * inv, o[qb][db][9 + 2 * u] * inv);
+            for (int g = 0; g < 4; ++g) {
+                u32x2_t w = {pack_bf16(o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv),
+                             pack_bf16(o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv)};
+                if (!real) w = u32x2_t{0u, 0u};             // pad row: +0.0
+                *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = w;
             }
-            if (!real) w0 = w1 = u32x4_t{0u, 0u, 0u, 0u};   // pad row: +0.0
-            *reinterpret_cast<u32x4_t*>(dst + 32 * db) = w0;
-            *reinterpret_cast<u32x4_t*>(dst + 32 * db + 8) = w1;
-        }
         if (p.lse && h == 0)
             p.lse[(int64_t)hq * p.lse_ld + q_start + qi] =
                 real ? (m_ref[qb] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;

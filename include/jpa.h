@@ -124,7 +124,8 @@ typedef struct jpa_row_plan {
  *   q         [Tq, Hq, D]  bf16, Tq = cu_q[batch]
  *   k_prefix  [Tp, Hkv, D] bf16, Tp = cu_prefix[batch]; v_prefix likewise
  *   k_suffix  [Ts, Hkv, D] bf16, Ts = cu_suffix_real[2*batch]; v_suffix likewise
- *   scale     softmax scale (finite, >= 0; head_dim**-0.5 in every DiT above)
+ *   scale     softmax scale (finite, >= 0; head_dim**-0.5 in every DiT above);
+ *             scale*log2(e) below 1e-30 is treated as 1e-30 (uniform weights)
  *   out       [Tq, Hq, D]  bf16, written entirely (pad rows as +0.0), rounded
  *             to nearest even; must not overlap any input
  *   lse       fp32 [Hq, Tq] (element (h, t) at lse[h*Tq + t]), natural log of
