@@ -44,6 +44,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "jpa_params.h"
 
@@ -93,6 +94,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Compile-time loop: f(std::integral_constant<int, 0>{}) ... f(<N-1>{}).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+template <int V>
+using ic = std::integral_constant<int, V>;
+
 __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
 }
@@ -106,6 +119,8 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     constexpr int kTile = kBN * D;           // elements of one K or V tile
     constexpr int kRowsPerOp = 512 / D;      // rows filled by one wave-wide 16 B/lane load
     constexpr int kOpsPerWave = kBN / kRowsPerOp / kWaves;
+    constexpr int kXSlots = kDS * kQB;       // QK MFMAs per 32-key unit
+    constexpr int kYSlots = kDB * 2 * kQB;   // PV MFMAs per 32-key unit
 
     // Three K tiles then three V tiles, all [key][d] (96 KB at D = 128).
     __shared__ __attribute__((aligned(16))) uint16_t lds[6 * kTile];
@@ -127,7 +142,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 31;                 // query column inside a 32-block
     const int h = lane >> 5;                 // lane half
 
@@ -175,8 +190,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         for (int ds = 0; ds < kDS; ++ds) qf[qb][ds] = __builtin_bit_cast(bf16x8_t, load16(src + 16 * ds));
     }
     // Register classes: Q fragments and the O accumulators live in AGPRs (only
-    // MFMAs touch them in the loop); scores live in VGPRs where the softmax
-    // VALU work reads them.  Empty asm statements pin the classes.
+    // MFMAs touch them in the loop); the softmax VALU work uses VGPRs.
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
@@ -188,49 +202,56 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     //      fetches the global chunk that belongs at its physical LDS slot,
     //      which realises the XOR swizzles.  Negative keys (the head of tile 0)
     //      re-read key 0; their scores are masked.  No pad slot is touched.
-    auto load_tile = [&](int t) {
-        const int slot = t % 3;
-        uint16_t* kdst = lds + slot * kTile;
-        uint16_t* vdst = lds + (3 + slot) * kTile;
-#pragma unroll
-        for (int i = 0; i < kOpsPerWave; ++i) {
-            const int row0 = (wave * kOpsPerWave + i) * kRowsPerOp;
-            const int row = row0 + lane / kCH;
-            const int pc = lane % kCH;
-            const int key = max(t * kBN - shift + row, 0);
-            const bool pre = key < P;
-            const uint16_t* gk = (pre ? kp + (p_row0 + key) * p.kp_ts : ks + (s_row0 + key) * p.ks_ts) +
-                                 ((pc ^ swz_k(row)) & (kCH - 1)) * 8;
-            const uint16_t* gv = (pre ? vp + (p_row0 + key) * p.vp_ts : vs + (s_row0 + key) * p.vs_ts) +
-                                 ((pc ^ (2 * (row & 3))) & (kCH - 1)) * 8;
-            __builtin_amdgcn_global_load_lds(gk, (__attribute__((address_space(3))) void*)(kdst + row0 * D),
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds(gv, (__attribute__((address_space(3))) void*)(vdst + row0 * D),
-                                             16, 0, 0);
-        }
+    auto dma_op = [&](int t, auto SLOT, int i) __attribute__((always_inline)) {
+        constexpr int slot = decltype(SLOT)::value;
+        const int row0 = (wave * kOpsPerWave + i) * kRowsPerOp;
+        const int row = row0 + lane / kCH;
+        const int pc = lane % kCH;
+        const int key = max(t * kBN - shift + row, 0);
+        const bool pre = key < P;
+        const uint16_t* gk = (pre ? kp + (p_row0 + key) * p.kp_ts : ks + (s_row0 + key) * p.ks_ts) +
+                             ((pc ^ swz_k(row)) & (kCH - 1)) * 8;
+        const uint16_t* gv = (pre ? vp + (p_row0 + key) * p.vp_ts : vs + (s_row0 + key) * p.vs_ts) +
+                             ((pc ^ (2 * (row & 3))) & (kCH - 1)) * 8;
+        __builtin_amdgcn_global_load_lds(gk, (__attribute__((address_space(3))) void*)(lds + slot * kTile + row0 * D),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(gv, (__attribute__((address_space(3))) void*)(lds + (3 + slot) * kTile + row0 * D),
+                                         16, 0, 0);
     };
 
-    // ---- per-lane LDS fragment addresses (loop invariant)
+    // ---- per-lane LDS fragment addresses (loop invariant; the tile slot and
+    //      the unit enter as immediate offsets)
     //  K (A operand of S^T = K Q^T): lane (j, h) reads row perm_k(j), 16-byte
     //  chunk 2*ds + h of the [key][d] tile.
     //  V (A operand of O^T = V^T P^T) comes from the [key][d] tile through
     //  ds_read_b64_tr_b16: in each 16-lane group, source lane 4k+q points at
     //  key row (.. + k), features 4q..4q+3 of the group's 16-feature block, and
     //  result lane i receives feature i of those 4 keys.  Two such reads give
-    //  a lane the 8 consecutive keys 16t + 8h .. +7 of one feature column.
+    //  a lane the 8 consecutive keys 16u + 8h .. +7 of one feature column.
     const int krow = perm_k(j);
-    int k_off[kDS];
+    const uint16_t* k_lane[kDS];
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds)
-        k_off[ds] = krow * D + (((2 * ds + h) ^ swz_k(krow)) & (kCH - 1)) * 8;
+        k_lane[ds] = lds + krow * D + (((2 * ds + h) ^ swz_k(krow)) & (kCH - 1)) * 8;
     const int tr_k = (lane & 15) >> 2;       // key offset supplied by this lane
     const int tr_q = lane & 3;               // 4-feature group supplied by this lane
     const int tr_half = (lane >> 4) & 1;     // which 16 features of the 32-block
-    const int v_row = (8 * h + tr_k) * D;
-    int v_col[kDB];
+    const uint16_t* v_lane[kDB];
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
-        v_col[db] = (((8 * db + 4 * tr_half + tr_q) ^ (4 * tr_k)) & (D / 4 - 1)) * 4;
+        v_lane[db] = lds + 3 * kTile + (8 * h + tr_k) * D +
+                     (((8 * db + 4 * tr_half + tr_q) ^ (4 * tr_k)) & (D / 4 - 1)) * 4;
+
+    auto read_k = [&](auto SLOT, auto KB, int ds) __attribute__((always_inline)) {
+        constexpr int off = decltype(SLOT)::value * kTile + decltype(KB)::value * 32 * D;
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(k_lane[ds] + off));
+    };
+    auto read_v = [&](auto SLOT, auto KB, int db, int u) __attribute__((always_inline)) {
+        const uint16_t* a = v_lane[db] + decltype(SLOT)::value * kTile + (decltype(KB)::value * 32 + 16 * u) * D;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a + 4 * D));
+        return __builtin_bit_cast(bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
 
     f32x16_t o[kQB][kDB];
     float m_ref[kQB], l_sum[kQB];
@@ -247,43 +268,9 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     }
     const float c = p.c;
 
-    // One "unit" = 32 keys of a tile (kb = 0 or 1).
-    // S^T = K Q^T for one unit, both query blocks (each K fragment feeds two MFMAs)
-    auto qk = [&](f32x16_t (&s)[kQB], int t, int kb) {
-        const uint16_t* base = lds + (t % 3) * kTile + kb * 32 * D;
-#pragma unroll
-        for (int ds = 0; ds < kDS; ++ds) {
-            const bf16x8_t kf = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const u32x4_t*>(base + k_off[ds]));
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb)
-                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ds],
-                                                                ds == 0 ? f32x16_t{} : s[qb], 0, 0, 0);
-        }
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) asm("" : "+v"(s[qb]));
-    };
-    // O^T += V^T P^T for one unit (each V fragment feeds two MFMAs)
-    auto pv = [&](int t, int kb, const bf16x8_t (&p0)[2], const bf16x8_t (&p1)[2]) {
-        const uint16_t* base = lds + (3 + t % 3) * kTile + kb * 32 * D + v_row;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const uint16_t* a = base + 16 * u * D + v_col[db];
-                const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4_t*)(a));
-                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4_t*)(a + 4 * D));
-                const bf16x8_t vf = __builtin_bit_cast(
-                    bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-                o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p0[u], o[0][db], 0, 0, 0);
-                o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p1[u], o[1][db], 0, 0, 0);
-            }
-    };
     // Scores of negative keys (head of tile 0) -> -FLT_MAX.  A finite value
     // keeps a fully masked unit NaN-free: its weights underflow to 0.
-    auto mask_head = [&](f32x16_t (&s)[kQB], int kb) {
+    auto mask_head = [&](f32x16_t (&s)[kQB], int kb) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const bool dead = kb * 32 + perm_k(8 * (r >> 2) + 4 * h + (r & 3)) < shift;
@@ -291,17 +278,21 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
             for (int qb = 0; qb < kQB; ++qb) s[qb][r] = dead ? -3.402823466e38f : s[qb][r];
         }
     };
+    // Row max over accumulator registers [r0, r1) of one query block.
+    auto part_max = [&](const f32x16_t& s, int r0, int r1, float init) __attribute__((always_inline)) {
+        float mx = init;
+#pragma unroll
+        for (int r = r0; r < r1; ++r) mx = fmaxf(mx, s[r]);
+        return mx;
+    };
     // Move the reference max of each query block when the unit's max exceeds
     // it by more than kTau (log2 units); returns whether any lane moved.
-    auto update_ref = [&](const f32x16_t (&s)[kQB], float (&alpha)[kQB]) {
+    auto decide = [&](const float (&mx)[kQB], float (&alpha)[kQB], bool valid) __attribute__((always_inline)) {
         bool any = false;
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
-            float mx = s[qb][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qb][r]);
-            const float mt = fmaxf(other_half_max(mx) * c, -1e30f);
-            const bool need = mt > m_ref[qb] + kTau;
+            const float mt = fmaxf(other_half_max(mx[qb]) * c, -1e30f);
+            const bool need = valid && mt > m_ref[qb] + kTau;
             const float mn = need ? mt : m_ref[qb];
             alpha[qb] = __builtin_amdgcn_exp2f(m_ref[qb] - mn);
             m_ref[qb] = mn;
@@ -309,7 +300,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         }
         return __builtin_amdgcn_ballot_w64(any) != 0;
     };
-    auto rescale = [&](const float (&alpha)[kQB]) {
+    auto rescale = [&](const float (&alpha)[kQB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
             l_sum[qb] *= alpha[qb];
@@ -319,83 +310,157 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
                 for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha[qb];
         }
     };
-    // P = 2^(S*c - m) for one query block of a unit, as two bf16 B-operand
-    // fragments (keys 16u + 8h .. +7); returns the fp32 sum of the weights
-    // (unrounded, so the LSE does not carry the bf16 rounding of P).
-    auto exp_pack = [&](const f32x16_t& s, float m, bf16x8_t (&pf)[2]) {
-        float lsum = 0.f;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            uint32_t pk[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const int r0 = 8 * u + 2 * w;
-                const float e0 = __builtin_amdgcn_exp2f(fmaf(s[r0], c, -m));
-                const float e1 = __builtin_amdgcn_exp2f(fmaf(s[r0 + 1], c, -m));
-                pk[w] = pack_bf16(e0, e1);
-                lsum += e0 + e1;
+    // One pair of weights 2^(S*c - m) of one query block: registers 2w, 2w+1.
+    auto exp_pair = [&](const f32x16_t& s, float m, int w, uint32_t& pk, float& lsum) __attribute__((always_inline)) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[2 * w], c, -m));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[2 * w + 1], c, -m));
+        pk = pack_bf16(e0, e1);
+        lsum += e0 + e1;     // fp32 sum of the unrounded weights (LSE precision)
+    };
+    auto pack_frags = [&](const uint32_t (&pk)[8], bf16x8_t (&pf)[2]) __attribute__((always_inline)) {
+        pf[0] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+        pf[1] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4], pk[5], pk[6], pk[7]});
+    };
+
+    // ---- One 32-key unit as a hand-placed instruction schedule.  Each slot
+    //      holds one MFMA (32 cycles on the matrix core) and a few VALU or LDS
+    //      instructions that issue while it runs; sched_barrier keeps the slots
+    //      apart.
+    //  X slots: QK^T MFMAs of the next unit (K tile KSN, half KBN) -> sn, with
+    //           the weights of the current unit's second query block.
+    //  Y slots: PV MFMAs of the current unit (V tile VS, half KBC), with the
+    //           max / reference update / first-block weights of the next unit.
+    //  The first two K fragments of every X phase are read at the end of the
+    //  previous Y phase (kpre), the first two V fragments at the end of X.
+    bf16x8_t kpre[2];
+    auto unit = [&](auto KSN, auto KBN, auto VS, auto KBC, auto KSNN, auto KBNN,
+                    f32x16_t (&sc)[kQB], f32x16_t (&sn)[kQB], const bf16x8_t (&pc0)[2],
+                    bf16x8_t (&pn0)[2], int dma_t, auto DMA_SLOT, auto DO_DMA, bool valid_next,
+                    auto MASK_NEXT) __attribute__((always_inline)) {
+        bf16x8_t kf[kDS];
+        kf[0] = kpre[0];
+        kf[1] = kpre[1];
+        bf16x8_t vf[kDB * 2];
+        uint32_t pk1[8];
+        float e_l1 = 0.f;
+        bf16x8_t p1[2];
+        // X phase
+        static_for<kXSlots>([&](auto I) __attribute__((always_inline)) {
+            constexpr int i = decltype(I)::value;
+            constexpr int ds = i / kQB, qb = i % kQB;
+            if constexpr (qb == 0 && ds + 2 < kDS) kf[ds + 2] = read_k(KSN, KBN, ds + 2);
+            sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[qb][ds],
+                                                             ds == 0 ? f32x16_t{} : sn[qb], 0, 0, 0);
+            // 8 weight pairs of the second query block spread over the slots
+            if constexpr (kXSlots >= 8) {
+                if constexpr (i % (kXSlots / 8) == 0) exp_pair(sc[1], m_ref[1], i / (kXSlots / 8), pk1[i / (kXSlots / 8)], e_l1);
+            } else {
+                exp_pair(sc[1], m_ref[1], 2 * i, pk1[2 * i], e_l1);
+                exp_pair(sc[1], m_ref[1], 2 * i + 1, pk1[2 * i + 1], e_l1);
             }
-            pf[u] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-        }
-        return lsum;
+            if constexpr (decltype(DO_DMA)::value && i % 2 == 1 && i / 2 < kOpsPerWave) dma_op(dma_t, DMA_SLOT, i / 2);
+            if constexpr (i == kXSlots - 4) vf[0] = read_v(VS, KBC, 0, 0);
+            if constexpr (i == kXSlots - 2) vf[1] = read_v(VS, KBC, 0, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        pack_frags(pk1, p1);
+        l_sum[1] += e_l1;
+        // Y phase
+        float mx[kQB];
+        float alpha[kQB];
+        bool any = false;
+        uint32_t pk0[8];
+        float ts0 = 0.f;
+        constexpr int kJobs0 = 2;                      // first slot with VALU work
+        static_for<kYSlots>([&](auto I) __attribute__((always_inline)) {
+            constexpr int i = decltype(I)::value;
+            constexpr int step = i / kQB, qb = i % kQB;     // step = (db, u)
+            constexpr int db = step / 2, u = step % 2;
+            if constexpr (qb == 0 && step + 2 < kDB * 2) vf[step + 2] = read_v(VS, KBC, (step + 2) / 2, (step + 2) % 2);
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[step], qb == 0 ? pc0[u] : p1[u], o[qb][db], 0, 0, 0);
+            // VALU jobs: 0 mask, 1..4 max halves, 5 decide, 6..13 weight pairs
+            constexpr int kN = 14;
+            constexpr int span = kYSlots - kJobs0 - 1;
+            static_for<kN>([&](auto J) __attribute__((always_inline)) {
+                constexpr int jb = decltype(J)::value;
+                constexpr int slot = kJobs0 + (jb * span) / kN;
+                if constexpr (slot == i) {
+                    if constexpr (jb == 0) {
+                        if constexpr (decltype(MASK_NEXT)::value) mask_head(sn, decltype(KBN)::value);
+                    } else if constexpr (jb == 1) mx[0] = part_max(sn[0], 0, 8, -INFINITY);
+                    else if constexpr (jb == 2) mx[0] = part_max(sn[0], 8, 16, mx[0]);
+                    else if constexpr (jb == 3) mx[1] = part_max(sn[1], 0, 8, -INFINITY);
+                    else if constexpr (jb == 4) mx[1] = part_max(sn[1], 8, 16, mx[1]);
+                    else if constexpr (jb == 5) any = decide(mx, alpha, valid_next);
+                    else exp_pair(sn[0], m_ref[0], jb - 6, pk0[jb - 6], ts0);
+                }
+            });
+            if constexpr (i == kYSlots - 3) kpre[0] = read_k(KSNN, KBNN, 0);
+            if constexpr (i == kYSlots - 1) kpre[1] = read_k(KSNN, KBNN, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        pack_frags(pk0, pn0);
+        // keep the weights in the Y slots (not sunk past the rare branch)
+        asm volatile("" : "+v"(pn0[0]), "+v"(pn0[1]), "+v"(ts0));
+        if (any) rescale(alpha);
+        l_sum[0] += valid_next ? ts0 : 0.f;
     };
 
     // ---- prologue: tiles 0 and 1 into LDS; scores, reference max and the
     //      first query block's weights of unit (0, 0).
     f32x16_t sA[kQB], sB[kQB];
-    bf16x8_t pA0[2], pB0[2], p1[2];
-    load_tile(0);
-    if (ntiles > 1) load_tile(1);
+    bf16x8_t pA0[2], pB0[2];
+    for (int i = 0; i < kOpsPerWave; ++i) {
+        dma_op(0, ic<0>{}, i);
+        dma_op(min(1, ntiles - 1), ic<1>{}, i);
+    }
     __syncthreads();
-    qk(sA, 0, 0);
+#pragma unroll
+    for (int ds = 0; ds < kDS; ++ds) {
+        const bf16x8_t kf = read_k(ic<0>{}, ic<0>{}, ds);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+            sA[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ds], ds == 0 ? f32x16_t{} : sA[qb], 0, 0, 0);
+    }
     mask_head(sA, 0);
     {
-        float alpha[kQB];
-        update_ref(sA, alpha);               // O and l are still zero
-        l_sum[0] = exp_pack(sA[0], m_ref[0], pA0);
+        float mx[kQB], alpha[kQB];
+        mx[0] = part_max(sA[0], 0, 16, -INFINITY);
+        mx[1] = part_max(sA[1], 0, 16, -INFINITY);
+        decide(mx, alpha, true);             // O and l are still zero: no rescale
+        uint32_t pk0[8];
+        float ts0 = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) exp_pair(sA[0], m_ref[0], w, pk0[w], ts0);
+        pack_frags(pk0, pA0);
+        l_sum[0] = ts0;
     }
+    kpre[0] = read_k(ic<0>{}, ic<1>{}, 0);
+    kpre[1] = read_k(ic<0>{}, ic<1>{}, 1);
 
-    // ---- steady state, per tile t (two units):
-    //   unit (t,0)  X: QK of unit (t,1)    || weights of (t,0), query block 1
-    //               Y: PV of unit (t,0)    || max of (t,1), reference update,
-    //                                          weights of (t,1), query block 0
-    //   unit (t,1)  X: QK of unit (t+1,0)  || weights of (t,1), query block 1
-    //               Y: PV of unit (t,1)    || max of (t+1,0), reference update,
-    //                                          weights of (t+1,0), query block 0
-    //   Tile t+2 is fetched at the start, one barrier at the end.  On the last
-    //   tile the look-ahead re-reads unit (t,0) (already counted, so it can
-    //   never move the reference) and its weights are dropped.
-    auto body = [&](int t, auto first) {
-        if (t + 2 < ntiles) load_tile(t + 2);
-        float alpha[kQB];
-        // unit (t,0)
-        qk(sB, t, 1);
-        l_sum[1] += exp_pack(sA[1], m_ref[1], p1);
-        if constexpr (decltype(first)::value) mask_head(sB, 1);
-        pv(t, 0, pA0, p1);
-        {
-            const bool any = update_ref(sB, alpha);
-            float ts0 = exp_pack(sB[0], m_ref[0], pB0);
-            asm volatile("" : "+v"(ts0), "+v"(pB0[0]), "+v"(pB0[1]));   // computed here, not after the branch
-            if (any) rescale(alpha);
-            l_sum[0] += ts0;
-        }
-        // unit (t,1)
-        const bool last = t + 1 == ntiles;
-        qk(sA, last ? t : t + 1, 0);
-        l_sum[1] += exp_pack(sB[1], m_ref[1], p1);
-        pv(t, 1, pB0, p1);
-        {
-            const bool any = update_ref(sA, alpha);
-            float ts0 = exp_pack(sA[0], m_ref[0], pA0);
-            asm volatile("" : "+v"(ts0), "+v"(pA0[0]), "+v"(pA0[1]));
-            if (any) rescale(alpha);
-            l_sum[0] += last ? 0.f : ts0;
-        }
+    // ---- one 64-key tile in LDS slot S: units (t,0) and (t,1); tile t+2 is
+    //      fetched into slot S+2 meanwhile (clamped to the last tile, so the
+    //      copy is always of real keys).  On the last tile the look-ahead of
+    //      unit (t,1) reads a stale slot; its reference update is suppressed
+    //      and its weights are never used.
+    auto body = [&](int t, auto S, auto FIRST) __attribute__((always_inline)) {
+        constexpr int s = decltype(S)::value;
+        constexpr int s1 = (s + 1) % 3, s2 = (s + 2) % 3;
+        unit(ic<s>{}, ic<1>{}, ic<s>{}, ic<0>{}, ic<s1>{}, ic<0>{}, sA, sB, pA0, pB0,
+             min(t + 2, ntiles - 1), ic<s2>{}, std::true_type{}, true, FIRST);
+        unit(ic<s1>{}, ic<0>{}, ic<s>{}, ic<1>{}, ic<s1>{}, ic<1>{}, sB, sA, pB0, pA0,
+             0, ic<s2>{}, std::false_type{}, t + 1 < ntiles, std::false_type{});
         __syncthreads();
     };
-    body(0, std::true_type{});
-    for (int t = 1; t < ntiles; ++t) body(t, std::false_type{});
+    body(0, ic<0>{}, std::true_type{});
+    int t = 1;
+    for (; t + 3 <= ntiles; t += 3) {
+        body(t, ic<1>{}, std::false_type{});
+        body(t + 1, ic<2>{}, std::false_type{});
+        body(t + 2, ic<0>{}, std::false_type{});
+    }
+    if (t < ntiles) body(t++, ic<1>{}, std::false_type{});
+    if (t < ntiles) body(t++, ic<2>{}, std::false_type{});
 
     // ---- epilogue: normalise, bf16 round-to-nearest-even, pad rows as zeros.
     //      O^T accumulator register r of lane half h is feature
