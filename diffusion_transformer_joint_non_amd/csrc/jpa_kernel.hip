@@ -22,7 +22,9 @@
 //   per lane, no staging registers) into natural [key][d] tiles; the V^T
 //   operand is read with the gfx950 LDS transpose load ds_read_b64_tr_b16.
 //   XOR swizzles of the 16-byte (K) and 8-byte (V) chunks keep the reads free
-//   of bank conflicts.  K and V are triple-buffered; one barrier per tile.
+//   of bank conflicts.  Four K and four V tile buffers, each its own LDS
+//   array: tile t+3 is fetched while tile t is computed, and the per-tile
+//   barrier only waits for the copy issued one tile earlier.
 // * Software pipeline inside each wave over 32-key units: the QK^T MFMAs of
 //   unit u+1 are issued alongside the exponentials of unit u (second query
 //   block), and the PV MFMAs of unit u alongside the row max and the first
@@ -106,6 +108,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
+// 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4).  Written as
+// inline asm so that the compiler does not track it; the kernel's own
+// s_waitcnt vmcnt(N) before each barrier orders it.  m0 holds the LDS base.
+__device__ __forceinline__ void lds_copy16(const void* gaddr, const void* lds_dst) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst;
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(gaddr), "{m0}"(m0v) : "memory");
+}
+
 __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
 }
@@ -122,8 +132,36 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     constexpr int kXSlots = kDS * kQB;       // QK MFMAs per 32-key unit
     constexpr int kYSlots = kDB * 2 * kQB;   // PV MFMAs per 32-key unit
 
-    // Three K tiles then three V tiles, all [key][d] (96 KB at D = 128).
-    __shared__ __attribute__((aligned(16))) uint16_t lds[6 * kTile];
+    // Barrier that lets the most recent tile prefetch (2*kOpsPerWave loads
+    // of this wave) stay in flight: s_waitcnt vmcnt(N) lgkmcnt(0); s_barrier.
+    // gfx9 s_waitcnt fields: vmcnt[3:0] bits 3:0, expcnt bits 6:4,
+    // lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14.
+    constexpr int kWaitVm = 2 * kOpsPerWave;
+    constexpr int kWaitImm = (kWaitVm & 15) | (7 << 4) | (0 << 8) | ((kWaitVm >> 4) << 14);
+    auto tile_barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitImm);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k0[kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k1[kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k2[kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k3[kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v0[kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v1[kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v2[kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v3[kTile];
+    auto kbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint16_t* {
+        constexpr int s = decltype(SLOT)::value;
+        if constexpr (s == 0) return lds_k0; else if constexpr (s == 1) return lds_k1;
+        else if constexpr (s == 2) return lds_k2; else return lds_k3;
+    };
+    auto vbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint16_t* {
+        constexpr int s = decltype(SLOT)::value;
+        if constexpr (s == 0) return lds_v0; else if constexpr (s == 1) return lds_v1;
+        else if constexpr (s == 2) return lds_v2; else return lds_v3;
+    };
 
     // ---- work item: XCD-grouped order over (head, row, query tile)
     const int nblk = gridDim.x;
@@ -172,6 +210,10 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     // key k < P is prefix token p_row0 + k; key k >= P is suffix slot s_row0 + k
     const int64_t p_row0 = p.rows[b].p_start;
     const int64_t s_row0 = (int64_t)p.rows[b].s_start - P;
+    // Token strides as scalars: a per-lane choice between them must select
+    // registers, never re-read the kernel arguments per lane.
+    int64_t kp_ts = p.kp_ts, ks_ts = p.ks_ts, vp_ts = p.vp_ts, vs_ts = p.vs_ts;
+    asm("" : "+s"(kp_ts), "+s"(ks_ts), "+s"(vp_ts), "+s"(vs_ts));
     // The key walk is shifted so that the tiles end exactly at Nk: only tile
     // 0 can be partial, and its missing keys are the negative indices.
     const int ntiles = (Nk + kBN - 1) / kBN;
@@ -209,14 +251,42 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         const int pc = lane % kCH;
         const int key = max(t * kBN - shift + row, 0);
         const bool pre = key < P;
-        const uint16_t* gk = (pre ? kp + (p_row0 + key) * p.kp_ts : ks + (s_row0 + key) * p.ks_ts) +
+        const uint16_t* gk = (pre ? kp + (p_row0 + key) * kp_ts : ks + (s_row0 + key) * ks_ts) +
                              ((pc ^ swz_k(row)) & (kCH - 1)) * 8;
-        const uint16_t* gv = (pre ? vp + (p_row0 + key) * p.vp_ts : vs + (s_row0 + key) * p.vs_ts) +
+        const uint16_t* gv = (pre ? vp + (p_row0 + key) * vp_ts : vs + (s_row0 + key) * vs_ts) +
                              ((pc ^ (2 * (row & 3))) & (kCH - 1)) * 8;
-        __builtin_amdgcn_global_load_lds(gk, (__attribute__((address_space(3))) void*)(lds + slot * kTile + row0 * D),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds(gv, (__attribute__((address_space(3))) void*)(lds + (3 + slot) * kTile + row0 * D),
-                                         16, 0, 0);
+        lds_copy16(gk, kbuf(SLOT) + row0 * D);
+        lds_copy16(gv, vbuf(SLOT) + row0 * D);
+    };
+    // Whole-tile copy.  When every key of tile t lies in one tensor (all tiles
+    // but the one straddling prefix and suffix, and the clamped head tile)
+    // the rows are a wave-uniform base (scalar arithmetic) plus a 32-bit
+    // per-lane offset; otherwise each lane forms its own row pointer.
+    const int lane_row = lane / kCH;
+    const int lane_pc = lane % kCH;
+    auto dma_tile = [&](int t, auto SLOT) __attribute__((always_inline)) {
+        constexpr int slot = decltype(SLOT)::value;
+        const int key0 = t * kBN - shift;
+        const bool all_suffix = key0 >= P;
+        const bool all_prefix = key0 >= 0 && key0 + kBN <= P;
+        if (all_suffix || all_prefix) {
+            const uint16_t* kb = all_suffix ? ks + (s_row0 + key0) * ks_ts : kp + (p_row0 + key0) * kp_ts;
+            const uint16_t* vb = all_suffix ? vs + (s_row0 + key0) * vs_ts : vp + (p_row0 + key0) * vp_ts;
+            const uint32_t krb = 2u * (uint32_t)(all_suffix ? ks_ts : kp_ts);
+            const uint32_t vrb = 2u * (uint32_t)(all_suffix ? vs_ts : vp_ts);
+#pragma unroll
+            for (int i = 0; i < kOpsPerWave; ++i) {
+                const int row0 = (wave * kOpsPerWave + i) * kRowsPerOp;
+                const int row = row0 + lane_row;
+                const uint32_t koff = (uint32_t)lane_row * krb + (((lane_pc ^ swz_k(row)) & (kCH - 1)) << 4);
+                const uint32_t voff = (uint32_t)lane_row * vrb + (((lane_pc ^ (2 * (row & 3))) & (kCH - 1)) << 4);
+                lds_copy16(reinterpret_cast<const char*>(kb + (int64_t)row0 * (krb / 2)) + koff, kbuf(SLOT) + row0 * D);
+                lds_copy16(reinterpret_cast<const char*>(vb + (int64_t)row0 * (vrb / 2)) + voff, vbuf(SLOT) + row0 * D);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kOpsPerWave; ++i) dma_op(t, SLOT, i);
+        }
     };
 
     // ---- per-lane LDS fragment addresses (loop invariant; the tile slot and
@@ -229,25 +299,24 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     //  result lane i receives feature i of those 4 keys.  Two such reads give
     //  a lane the 8 consecutive keys 16u + 8h .. +7 of one feature column.
     const int krow = perm_k(j);
-    const uint16_t* k_lane[kDS];
+    int k_lane[kDS];
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds)
-        k_lane[ds] = lds + krow * D + (((2 * ds + h) ^ swz_k(krow)) & (kCH - 1)) * 8;
+        k_lane[ds] = krow * D + (((2 * ds + h) ^ swz_k(krow)) & (kCH - 1)) * 8;
     const int tr_k = (lane & 15) >> 2;       // key offset supplied by this lane
     const int tr_q = lane & 3;               // 4-feature group supplied by this lane
     const int tr_half = (lane >> 4) & 1;     // which 16 features of the 32-block
-    const uint16_t* v_lane[kDB];
+    int v_lane[kDB];
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
-        v_lane[db] = lds + 3 * kTile + (8 * h + tr_k) * D +
-                     (((8 * db + 4 * tr_half + tr_q) ^ (4 * tr_k)) & (D / 4 - 1)) * 4;
+        v_lane[db] = (8 * h + tr_k) * D + (((8 * db + 4 * tr_half + tr_q) ^ (4 * tr_k)) & (D / 4 - 1)) * 4;
 
     auto read_k = [&](auto SLOT, auto KB, int ds) __attribute__((always_inline)) {
-        constexpr int off = decltype(SLOT)::value * kTile + decltype(KB)::value * 32 * D;
-        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(k_lane[ds] + off));
+        constexpr int off = decltype(KB)::value * 32 * D;
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(kbuf(SLOT) + k_lane[ds] + off));
     };
     auto read_v = [&](auto SLOT, auto KB, int db, int u) __attribute__((always_inline)) {
-        const uint16_t* a = v_lane[db] + decltype(SLOT)::value * kTile + (decltype(KB)::value * 32 + 16 * u) * D;
+        const uint16_t* a = vbuf(SLOT) + v_lane[db] + (decltype(KB)::value * 32 + 16 * u) * D;
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a));
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a + 4 * D));
         return __builtin_bit_cast(bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
@@ -335,8 +404,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     bf16x8_t kpre[2];
     auto unit = [&](auto KSN, auto KBN, auto VS, auto KBC, auto KSNN, auto KBNN,
                     f32x16_t (&sc)[kQB], f32x16_t (&sn)[kQB], const bf16x8_t (&pc0)[2],
-                    bf16x8_t (&pn0)[2], int dma_t, auto DMA_SLOT, auto DO_DMA, bool valid_next,
-                    auto MASK_NEXT) __attribute__((always_inline)) {
+                    bf16x8_t (&pn0)[2], bool valid_next, auto MASK_NEXT) __attribute__((always_inline)) {
         bf16x8_t kf[kDS];
         kf[0] = kpre[0];
         kf[1] = kpre[1];
@@ -358,7 +426,6 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
                 exp_pair(sc[1], m_ref[1], 2 * i, pk1[2 * i], e_l1);
                 exp_pair(sc[1], m_ref[1], 2 * i + 1, pk1[2 * i + 1], e_l1);
             }
-            if constexpr (decltype(DO_DMA)::value && i % 2 == 1 && i / 2 < kOpsPerWave) dma_op(dma_t, DMA_SLOT, i / 2);
             if constexpr (i == kXSlots - 4) vf[0] = read_v(VS, KBC, 0, 0);
             if constexpr (i == kXSlots - 2) vf[1] = read_v(VS, KBC, 0, 1);
             __builtin_amdgcn_sched_barrier(0);
@@ -410,11 +477,11 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     //      first query block's weights of unit (0, 0).
     f32x16_t sA[kQB], sB[kQB];
     bf16x8_t pA0[2], pB0[2];
-    for (int i = 0; i < kOpsPerWave; ++i) {
-        dma_op(0, ic<0>{}, i);
-        dma_op(min(1, ntiles - 1), ic<1>{}, i);
-    }
-    __syncthreads();
+    dma_tile(0, ic<0>{});
+    dma_tile(min(1, ntiles - 1), ic<1>{});
+    dma_tile(min(2, ntiles - 1), ic<2>{});
+    // tiles 0 and 1 must have landed; tile 2 may still be in flight
+    tile_barrier();
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds) {
         const bf16x8_t kf = read_k(ic<0>{}, ic<0>{}, ds);
@@ -438,29 +505,36 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     kpre[0] = read_k(ic<0>{}, ic<1>{}, 0);
     kpre[1] = read_k(ic<0>{}, ic<1>{}, 1);
 
-    // ---- one 64-key tile in LDS slot S: units (t,0) and (t,1); tile t+2 is
-    //      fetched into slot S+2 meanwhile (clamped to the last tile, so the
-    //      copy is always of real keys).  On the last tile the look-ahead of
-    //      unit (t,1) reads a stale slot; its reference update is suppressed
-    //      and its weights are never used.
+    // ---- one 64-key tile in buffer S (of 4): units (t,0) and (t,1); tile t+3
+    //      is fetched into buffer S+3 meanwhile (clamped to the last tile, so
+    //      the copy is always of real keys).  On the last tile the look-ahead
+    //      of unit (t,1) reads a stale buffer; its reference update is
+    //      suppressed and its weights are never used.
     auto body = [&](int t, auto S, auto FIRST) __attribute__((always_inline)) {
         constexpr int s = decltype(S)::value;
-        constexpr int s1 = (s + 1) % 3, s2 = (s + 2) % 3;
-        unit(ic<s>{}, ic<1>{}, ic<s>{}, ic<0>{}, ic<s1>{}, ic<0>{}, sA, sB, pA0, pB0,
-             min(t + 2, ntiles - 1), ic<s2>{}, std::true_type{}, true, FIRST);
+        constexpr int s1 = (s + 1) % 4, s3 = (s + 3) % 4;
+        dma_tile(min(t + 3, ntiles - 1), ic<s3>{});
+        unit(ic<s>{}, ic<1>{}, ic<s>{}, ic<0>{}, ic<s1>{}, ic<0>{}, sA, sB, pA0, pB0, true, FIRST);
         unit(ic<s1>{}, ic<0>{}, ic<s>{}, ic<1>{}, ic<s1>{}, ic<1>{}, sB, sA, pB0, pA0,
-             0, ic<s2>{}, std::false_type{}, t + 1 < ntiles, std::false_type{});
-        __syncthreads();
+             t + 1 < ntiles, std::false_type{});
+        // Tiles up to t+2 must have landed before the barrier (tile t+2 is
+        // first read in the next tile); this tile's own prefetch (t+3, the
+        // last kOpsPerWave*2 loads) may stay in flight.
+        tile_barrier();
     };
     body(0, ic<0>{}, std::true_type{});
     int t = 1;
-    for (; t + 3 <= ntiles; t += 3) {
+    for (; t + 4 <= ntiles; t += 4) {
         body(t, ic<1>{}, std::false_type{});
         body(t + 1, ic<2>{}, std::false_type{});
-        body(t + 2, ic<0>{}, std::false_type{});
+        body(t + 2, ic<3>{}, std::false_type{});
+        body(t + 3, ic<0>{}, std::false_type{});
     }
     if (t < ntiles) body(t++, ic<1>{}, std::false_type{});
     if (t < ntiles) body(t++, ic<2>{}, std::false_type{});
+    if (t < ntiles) body(t++, ic<3>{}, std::false_type{});
+    // No tile copy may still be landing in LDS when the wave ends.
+    __builtin_amdgcn_s_waitcnt(0);
 
     // ---- epilogue: normalise, bf16 round-to-nearest-even, pad rows as zeros.
     //      O^T accumulator register r of lane half h is feature
