@@ -31,6 +31,8 @@ HIPCC_FLAGS = [
     # no packed fp32 VALU instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # MFMA results in VGPRs: the softmax reads the scores with no AGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -26,18 +26,20 @@
 //   array: tile t+3 is fetched while tile t is computed, and the per-tile
 //   barrier only waits for the copy issued one tile earlier.
 // * Software pipeline inside each wave over 32-key units: the QK^T MFMAs of
-//   unit u+1 are issued alongside the exponentials of unit u (second query
-//   block), and the PV MFMAs of unit u alongside the row max and the first
-//   query block's exponentials of unit u+1.
+//   unit u+1 are issued alongside the weights of unit u (second query
+//   block), and the PV MFMAs of unit u alongside the first query block's
+//   weights of unit u+1, one score register per MFMA slot.
 // * The key loop walks one index space [0, P_b + R_b): a key below P_b is
 //   read from the prefix tensor, the rest from the suffix tensor, per row,
 //   so the two tensors are never concatenated.  The tile grid is shifted so
 //   it ends exactly at P_b + R_b: only the first tile is partial (its head
 //   is masked) and no pad slot is ever loaded.
-// * Online softmax in the log2 domain, fp32, with a lazy rescale: the running
-//   reference max only moves when a tile's max exceeds it by more than 8
-//   (so P <= 2^8 and fp32 accumulators are safe), which skips the O rescale
-//   on almost every tile.
+// * Online softmax in the log2 domain, fp32, with a lazy rescale: weights
+//   are formed against a running reference without computing the unit's max;
+//   only when a lane's partial sum exceeds 2^8 does the wave move the
+//   reference to the unit's max, rescale O and form the weights again (so
+//   P <= 2^8 and the fp32 accumulators are safe).  The common path has no
+//   row max at all and almost never rescales.
 // * Work items are mapped so that the workgroups resident on one XCD (blocks
 //   are dealt round-robin over the 8 XCDs) cover consecutive query tiles of
 //   the same head, which then stream the same K/V through that XCD's L2.
@@ -66,7 +68,7 @@ constexpr int kQB = 2;                       // 32-query blocks per wave
 constexpr int kBM = kWaves * kQB * 32;       // query rows per workgroup
 constexpr int kBN = 64;                      // keys per tile
 constexpr int kKB = kBN / 32;                // 32-key blocks per tile
-constexpr float kTau = 8.0f;                 // lazy-rescale threshold (log2 units)
+constexpr float kBound = 256.0f;             // largest weight let into the PV product (2^8)
 
 static_assert(kBM == JPA_BLOCK_M, "host and kernel tile height differ");
 
@@ -347,48 +349,67 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
             for (int qb = 0; qb < kQB; ++qb) s[qb][r] = dead ? -3.402823466e38f : s[qb][r];
         }
     };
-    // Row max over accumulator registers [r0, r1) of one query block.
-    auto part_max = [&](const f32x16_t& s, int r0, int r1, float init) __attribute__((always_inline)) {
-        float mx = init;
+    // Row max of one query block over one 32-key unit (both lane halves), in
+    // log2 units, floored at -1e30 so that a fully masked unit stays finite.
+    auto unit_max = [&](const f32x16_t& s) __attribute__((always_inline)) {
+        float mx = s[0];
 #pragma unroll
-        for (int r = r0; r < r1; ++r) mx = fmaxf(mx, s[r]);
-        return mx;
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        return fmaxf(other_half_max(mx) * c, -1e30f);
     };
-    // Move the reference max of each query block when the unit's max exceeds
-    // it by more than kTau (log2 units); returns whether any lane moved.
-    auto decide = [&](const float (&mx)[kQB], float (&alpha)[kQB], bool valid) __attribute__((always_inline)) {
-        bool any = false;
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-            const float mt = fmaxf(other_half_max(mx[qb]) * c, -1e30f);
-            const bool need = valid && mt > m_ref[qb] + kTau;
-            const float mn = need ? mt : m_ref[qb];
-            alpha[qb] = __builtin_amdgcn_exp2f(m_ref[qb] - mn);
-            m_ref[qb] = mn;
-            any |= need;
-        }
-        return __builtin_amdgcn_ballot_w64(any) != 0;
+    // Weights 2^(S*c - m) of one query block in one unit, one accumulator
+    // register per step so that they spread evenly over the MFMA slots: step
+    // r forms weight r, adds weight r-1 to the lane's partial sum (fp32, of
+    // the unrounded weights: LSE precision) and, every second step, packs two
+    // weights to bf16 for the PV product.
+    struct Weights {
+        float e[16];
+        float part;
+        uint32_t pk[8];
     };
-    auto rescale = [&](const float (&alpha)[kQB]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-            l_sum[qb] *= alpha[qb];
-#pragma unroll
-            for (int db = 0; db < kDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha[qb];
-        }
+    auto w_step = [&](const f32x16_t& s, float m, Weights& w, auto R) __attribute__((always_inline)) {
+        constexpr int r = decltype(R)::value;
+        w.e[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m));
+        if constexpr (r == 1) w.part = w.e[0];
+        if constexpr (r >= 2) w.part += w.e[r - 1];
+        if constexpr (r >= 2 && (r & 1) == 0) w.pk[r / 2 - 1] = pack_bf16(w.e[r - 2], w.e[r - 1]);
     };
-    // One pair of weights 2^(S*c - m) of one query block: registers 2w, 2w+1.
-    auto exp_pair = [&](const f32x16_t& s, float m, int w, uint32_t& pk, float& lsum) __attribute__((always_inline)) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[2 * w], c, -m));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[2 * w + 1], c, -m));
-        pk = pack_bf16(e0, e1);
-        lsum += e0 + e1;     // fp32 sum of the unrounded weights (LSE precision)
+    auto w_tail = [&](Weights& w) __attribute__((always_inline)) {
+        w.part += w.e[15];
+        w.pk[7] = pack_bf16(w.e[14], w.e[15]);
+    };
+    auto w_all = [&](const f32x16_t& s, float m, Weights& w) __attribute__((always_inline)) {
+        static_for<16>([&](auto R) __attribute__((always_inline)) { w_step(s, m, w, R); });
+        w_tail(w);
     };
     auto pack_frags = [&](const uint32_t (&pk)[8], bf16x8_t (&pf)[2]) __attribute__((always_inline)) {
         pf[0] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
         pf[1] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[4], pk[5], pk[6], pk[7]});
+    };
+    // Lazy rescale.  Weights are formed against the running reference m_ref
+    // without looking at the unit's max first; only when some lane's partial
+    // sum exceeds 2^8 (a weight may then exceed 2^8, or be inf) does the wave
+    // move the reference up to the unit's max, rescale that block's O and l,
+    // and form the weights again.  So every weight that reaches the PV
+    // product is <= 2^8, and m_ref stays within 8 (log2 units) of the running
+    // max.  Then the lane sum is added to l.
+    auto settle = [&](auto QB, const f32x16_t& s, Weights& w, bool valid) __attribute__((always_inline)) {
+        constexpr int qb = decltype(QB)::value;
+        // the common-path weights are formed before the branch, in the slots
+        asm volatile("" : "+v"(w.part), "+v"(w.pk[0]), "+v"(w.pk[1]), "+v"(w.pk[2]), "+v"(w.pk[3]),
+                     "+v"(w.pk[4]), "+v"(w.pk[5]), "+v"(w.pk[6]), "+v"(w.pk[7]));
+        if (__builtin_amdgcn_ballot_w64(valid && w.part > kBound) != 0) {
+            const float mn = fmaxf(m_ref[qb], unit_max(s));
+            const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - mn);
+            m_ref[qb] = mn;
+            l_sum[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < kDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+            w_all(s, mn, w);
+        }
+        l_sum[qb] += valid ? w.part : 0.f;
     };
 
     // ---- One 32-key unit as a hand-placed instruction schedule.  Each slot
@@ -398,7 +419,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     //  X slots: QK^T MFMAs of the next unit (K tile KSN, half KBN) -> sn, with
     //           the weights of the current unit's second query block.
     //  Y slots: PV MFMAs of the current unit (V tile VS, half KBC), with the
-    //           max / reference update / first-block weights of the next unit.
+    //           weights of the next unit's first query block.
     //  The first two K fragments of every X phase are read at the end of the
     //  previous Y phase (kpre), the first two V fragments at the end of X.
     bf16x8_t kpre[2];
@@ -409,9 +430,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         kf[0] = kpre[0];
         kf[1] = kpre[1];
         bf16x8_t vf[kDB * 2];
-        uint32_t pk1[8];
-        float e_l1 = 0.f;
-        bf16x8_t p1[2];
+        Weights w1;
         // X phase
         static_for<kXSlots>([&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
@@ -419,62 +438,40 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
             if constexpr (qb == 0 && ds + 2 < kDS) kf[ds + 2] = read_k(KSN, KBN, ds + 2);
             sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[qb][ds],
                                                              ds == 0 ? f32x16_t{} : sn[qb], 0, 0, 0);
-            // 8 weight pairs of the second query block spread over the slots
-            if constexpr (kXSlots >= 8) {
-                if constexpr (i % (kXSlots / 8) == 0) exp_pair(sc[1], m_ref[1], i / (kXSlots / 8), pk1[i / (kXSlots / 8)], e_l1);
-            } else {
-                exp_pair(sc[1], m_ref[1], 2 * i, pk1[2 * i], e_l1);
-                exp_pair(sc[1], m_ref[1], 2 * i + 1, pk1[2 * i + 1], e_l1);
-            }
+            static_for<16>([&](auto R) __attribute__((always_inline)) {
+                if constexpr (decltype(R)::value * kXSlots / 16 == i) w_step(sc[1], m_ref[1], w1, R);
+            });
             if constexpr (i == kXSlots - 4) vf[0] = read_v(VS, KBC, 0, 0);
             if constexpr (i == kXSlots - 2) vf[1] = read_v(VS, KBC, 0, 1);
             __builtin_amdgcn_sched_barrier(0);
         });
-        pack_frags(pk1, p1);
-        l_sum[1] += e_l1;
+        w_tail(w1);
+        settle(ic<1>{}, sc[1], w1, true);
+        bf16x8_t p1[2];
+        pack_frags(w1.pk, p1);
         // Y phase
-        float mx[kQB];
-        float alpha[kQB];
-        bool any = false;
-        uint32_t pk0[8];
-        float ts0 = 0.f;
-        constexpr int kJobs0 = 2;                      // first slot with VALU work
+        Weights w0;
         static_for<kYSlots>([&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
             constexpr int step = i / kQB, qb = i % kQB;     // step = (db, u)
             constexpr int db = step / 2, u = step % 2;
             if constexpr (qb == 0 && step + 2 < kDB * 2) vf[step + 2] = read_v(VS, KBC, (step + 2) / 2, (step + 2) % 2);
             o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[step], qb == 0 ? pc0[u] : p1[u], o[qb][db], 0, 0, 0);
-            // VALU jobs: 0 mask, 1..4 max halves, 5 decide, 6..13 weight pairs
-            constexpr int kN = 14;
-            constexpr int span = kYSlots - kJobs0 - 1;
-            static_for<kN>([&](auto J) __attribute__((always_inline)) {
-                constexpr int jb = decltype(J)::value;
-                constexpr int slot = kJobs0 + (jb * span) / kN;
-                if constexpr (slot == i) {
-                    if constexpr (jb == 0) {
-                        if constexpr (decltype(MASK_NEXT)::value) mask_head(sn, decltype(KBN)::value);
-                    } else if constexpr (jb == 1) mx[0] = part_max(sn[0], 0, 8, -INFINITY);
-                    else if constexpr (jb == 2) mx[0] = part_max(sn[0], 8, 16, mx[0]);
-                    else if constexpr (jb == 3) mx[1] = part_max(sn[1], 0, 8, -INFINITY);
-                    else if constexpr (jb == 4) mx[1] = part_max(sn[1], 8, 16, mx[1]);
-                    else if constexpr (jb == 5) any = decide(mx, alpha, valid_next);
-                    else exp_pair(sn[0], m_ref[0], jb - 6, pk0[jb - 6], ts0);
-                }
+            if constexpr (i == 0 && decltype(MASK_NEXT)::value) mask_head(sn, decltype(KBN)::value);
+            static_for<16>([&](auto R) __attribute__((always_inline)) {
+                if constexpr (decltype(R)::value * kYSlots / 16 == i) w_step(sn[0], m_ref[0], w0, R);
             });
             if constexpr (i == kYSlots - 3) kpre[0] = read_k(KSNN, KBNN, 0);
             if constexpr (i == kYSlots - 1) kpre[1] = read_k(KSNN, KBNN, 1);
             __builtin_amdgcn_sched_barrier(0);
         });
-        pack_frags(pk0, pn0);
-        // keep the weights in the Y slots (not sunk past the rare branch)
-        asm volatile("" : "+v"(pn0[0]), "+v"(pn0[1]), "+v"(ts0));
-        if (any) rescale(alpha);
-        l_sum[0] += valid_next ? ts0 : 0.f;
+        w_tail(w0);
+        settle(ic<0>{}, sn[0], w0, valid_next);
+        pack_frags(w0.pk, pn0);
     };
 
-    // ---- prologue: tiles 0 and 1 into LDS; scores, reference max and the
-    //      first query block's weights of unit (0, 0).
+    // ---- prologue: tiles 0..2 into LDS; scores, reference max and the first
+    //      query block's weights of unit (0, 0).
     f32x16_t sA[kQB], sB[kQB];
     bf16x8_t pA0[2], pB0[2];
     dma_tile(0, ic<0>{});
@@ -490,17 +487,13 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
             sA[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ds], ds == 0 ? f32x16_t{} : sA[qb], 0, 0, 0);
     }
     mask_head(sA, 0);
+    m_ref[0] = unit_max(sA[0]);
+    m_ref[1] = unit_max(sA[1]);
     {
-        float mx[kQB], alpha[kQB];
-        mx[0] = part_max(sA[0], 0, 16, -INFINITY);
-        mx[1] = part_max(sA[1], 0, 16, -INFINITY);
-        decide(mx, alpha, true);             // O and l are still zero: no rescale
-        uint32_t pk0[8];
-        float ts0 = 0.f;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) exp_pair(sA[0], m_ref[0], w, pk0[w], ts0);
-        pack_frags(pk0, pA0);
-        l_sum[0] = ts0;
+        Weights w0;
+        w_all(sA[0], m_ref[0], w0);          // every weight <= 1 here
+        pack_frags(w0.pk, pA0);
+        l_sum[0] = w0.part;
     }
     kpre[0] = read_k(ic<0>{}, ic<1>{}, 0);
     kpre[1] = read_k(ic<0>{}, ic<1>{}, 1);
