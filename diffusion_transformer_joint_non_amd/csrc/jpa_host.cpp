@@ -55,7 +55,12 @@ jpa_status check_segments(int32_t batch, const int32_t* cu_q, const int32_t* cu_
     return JPA_OK;
 }
 
-jpa_status check_tensor(const jpa_tensor* t, int64_t tokens, int32_t heads, int32_t head_dim) {
+// K/V rows are addressed as a 32-bit multiple of the token stride in bytes
+// computed with a 24-bit multiply: token strides must stay below 2^23 elements.
+constexpr int64_t kMaxKvTokenStride = int64_t(1) << 23;
+
+jpa_status check_tensor(const jpa_tensor* t, int64_t tokens, int32_t heads, int32_t head_dim,
+                        bool kv = false) {
     if (!t) return JPA_ERR_NULL;
     if (t->dtype != JPA_DTYPE_BF16) return JPA_ERR_DTYPE;
     if (t->head_dim != head_dim || t->heads != heads || t->tokens != tokens) return JPA_ERR_SHAPE;
@@ -64,6 +69,7 @@ jpa_status check_tensor(const jpa_tensor* t, int64_t tokens, int32_t heads, int3
     if (t->token_stride % 8 != 0 || t->head_stride % 8 != 0) return JPA_ERR_LAYOUT;
     if (t->head_stride < t->head_dim) return JPA_ERR_LAYOUT;
     if (t->token_stride < (int64_t)t->heads * t->head_stride) return JPA_ERR_LAYOUT;
+    if (kv && t->token_stride >= kMaxKvTokenStride) return JPA_ERR_LAYOUT;
     return JPA_OK;
 }
 
@@ -82,10 +88,10 @@ jpa_status validate(const jpa_tensor* q, const jpa_tensor* k_prefix, const jpa_t
     const int64_t tq = cu_q[batch], tp = cu_prefix[batch], ts = cu_suffix_real[2 * batch];
     if ((st = check_tensor(q, tq, hq, d)) != JPA_OK) return st;
     if ((st = check_tensor(out, tq, hq, d)) != JPA_OK) return st;
-    if ((st = check_tensor(k_prefix, tp, hkv, d)) != JPA_OK) return st;
-    if ((st = check_tensor(v_prefix, tp, hkv, d)) != JPA_OK) return st;
-    if ((st = check_tensor(k_suffix, ts, hkv, d)) != JPA_OK) return st;
-    if ((st = check_tensor(v_suffix, ts, hkv, d)) != JPA_OK) return st;
+    if ((st = check_tensor(k_prefix, tp, hkv, d, true)) != JPA_OK) return st;
+    if ((st = check_tensor(v_prefix, tp, hkv, d, true)) != JPA_OK) return st;
+    if ((st = check_tensor(k_suffix, ts, hkv, d, true)) != JPA_OK) return st;
+    if ((st = check_tensor(v_suffix, ts, hkv, d, true)) != JPA_OK) return st;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JPA_ERR_LAYOUT;
     return JPA_OK;
 }

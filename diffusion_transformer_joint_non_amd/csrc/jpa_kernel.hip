@@ -23,8 +23,9 @@
 //   operand is read with the gfx950 LDS transpose load ds_read_b64_tr_b16.
 //   XOR swizzles of the 16-byte (K) and 8-byte (V) chunks keep the reads free
 //   of bank conflicts.  Four K and four V tile buffers, each its own LDS
-//   array: tile t+3 is fetched while tile t is computed, and the per-tile
-//   barrier only waits for the copy issued one tile earlier.
+//   array: tile t+3 is fetched while tile t is computed (its loads issued
+//   from the MFMA slots), and the per-tile barrier only waits for the copy
+//   issued one tile earlier.
 // * Software pipeline inside each wave over 32-key units: the QK^T MFMAs of
 //   unit u+1 are issued alongside the weights of unit u (second query
 //   block), and the PV MFMAs of unit u alongside the first query block's
@@ -118,6 +119,19 @@ __device__ __forceinline__ void lds_copy16(const void* gaddr, const void* lds_ds
     asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(gaddr), "{m0}"(m0v) : "memory");
 }
 
+// Same copy from a wave-uniform base address plus a 32-bit per-lane offset.
+__device__ __forceinline__ void lds_copy16_s(uintptr_t sbase, uint32_t voff, const void* lds_dst) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst;
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(m0v) : "memory");
+}
+
+// A wave-uniform 64-bit value in scalar registers.
+__device__ __forceinline__ uintptr_t uniform64(uintptr_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return ((uintptr_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
 }
@@ -133,6 +147,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     constexpr int kOpsPerWave = kBN / kRowsPerOp / kWaves;
     constexpr int kXSlots = kDS * kQB;       // QK MFMAs per 32-key unit
     constexpr int kYSlots = kDB * 2 * kQB;   // PV MFMAs per 32-key unit
+    static_assert(kXSlots / 2 == 2 * kOpsPerWave, "one copy job per odd X slot");
 
     // Barrier that lets the most recent tile prefetch (2*kOpsPerWave loads
     // of this wave) stay in flight: s_waitcnt vmcnt(N) lgkmcnt(0); s_barrier.
@@ -242,12 +257,20 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
 
     // ---- global -> LDS tile loads, 16 bytes per lane straight into LDS
     //      (global_load_lds_dwordx4: lane l of a wave lands at base + 16*l).
-    //      A wave instruction fills kRowsPerOp consecutive key rows; each lane
-    //      fetches the global chunk that belongs at its physical LDS slot,
-    //      which realises the XOR swizzles.  Negative keys (the head of tile 0)
-    //      re-read key 0; their scores are masked.  No pad slot is touched.
+    //      A wave instruction (an "op") fills kRowsPerOp consecutive key rows
+    //      of the tile; each lane fetches the global chunk that belongs at its
+    //      physical LDS slot, which realises the XOR swizzles.  No pad slot is
+    //      ever touched.
+    //  Common case, every key of the tile in one tensor: a scalar tile base
+    //  per tensor plus a 32-bit per-lane offset whose row is clamped to the
+    //  tile's valid rows (the head of tile 0 re-reads its first real key;
+    //  those scores are masked).  Three VALU instructions per K/V pair of
+    //  loads, issued from the MFMA slots of the tile before.
+    //  The one tile per batch row that straddles prefix and suffix is copied
+    //  by a general per-lane path before its unit; its slot loads then re-read
+    //  a valid row into a scratch LDS line that nothing reads.
+    __shared__ __attribute__((aligned(16))) uint16_t lds_scratch[512];
     auto dma_op = [&](int t, auto SLOT, int i) __attribute__((always_inline)) {
-        constexpr int slot = decltype(SLOT)::value;
         const int row0 = (wave * kOpsPerWave + i) * kRowsPerOp;
         const int row = row0 + lane / kCH;
         const int pc = lane % kCH;
@@ -260,35 +283,63 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         lds_copy16(gk, kbuf(SLOT) + row0 * D);
         lds_copy16(gv, vbuf(SLOT) + row0 * D);
     };
-    // Whole-tile copy.  When every key of tile t lies in one tensor (all tiles
-    // but the one straddling prefix and suffix, and the clamped head tile)
-    // the rows are a wave-uniform base (scalar arithmetic) plus a 32-bit
-    // per-lane offset; otherwise each lane forms its own row pointer.
     const int lane_row = lane / kCH;
     const int lane_pc = lane % kCH;
-    auto dma_tile = [&](int t, auto SLOT) __attribute__((always_inline)) {
-        constexpr int slot = decltype(SLOT)::value;
-        const int key0 = t * kBN - shift;
-        const bool all_suffix = key0 >= P;
-        const bool all_prefix = key0 >= 0 && key0 + kBN <= P;
-        if (all_suffix || all_prefix) {
-            const uint16_t* kb = all_suffix ? ks + (s_row0 + key0) * ks_ts : kp + (p_row0 + key0) * kp_ts;
-            const uint16_t* vb = all_suffix ? vs + (s_row0 + key0) * vs_ts : vp + (p_row0 + key0) * vp_ts;
-            const uint32_t krb = 2u * (uint32_t)(all_suffix ? ks_ts : kp_ts);
-            const uint32_t vrb = 2u * (uint32_t)(all_suffix ? vs_ts : vp_ts);
+    int r_lane[kOpsPerWave];            // tile row of this lane in op i
+    uint32_t kch[kOpsPerWave];          // byte offset of this lane's K chunk in op i
 #pragma unroll
-            for (int i = 0; i < kOpsPerWave; ++i) {
-                const int row0 = (wave * kOpsPerWave + i) * kRowsPerOp;
-                const int row = row0 + lane_row;
-                const uint32_t koff = (uint32_t)lane_row * krb + (((lane_pc ^ swz_k(row)) & (kCH - 1)) << 4);
-                const uint32_t voff = (uint32_t)lane_row * vrb + (((lane_pc ^ (2 * (row & 3))) & (kCH - 1)) << 4);
-                lds_copy16(reinterpret_cast<const char*>(kb + (int64_t)row0 * (krb / 2)) + koff, kbuf(SLOT) + row0 * D);
-                lds_copy16(reinterpret_cast<const char*>(vb + (int64_t)row0 * (vrb / 2)) + voff, vbuf(SLOT) + row0 * D);
-            }
+    for (int i = 0; i < kOpsPerWave; ++i) {
+        r_lane[i] = (wave * kOpsPerWave + i) * kRowsPerOp + lane_row;
+        kch[i] = (uint32_t)((lane_pc ^ swz_k(r_lane[i])) & (kCH - 1)) << 4;
+    }
+    // V chunk: op rows start at multiples of 4, so row & 3 == lane_row & 3
+    const uint32_t vch = (uint32_t)((lane_pc ^ (2 * (lane_row & 3))) & (kCH - 1)) << 4;
+
+    struct TilePlan {
+        uintptr_t kb, vb;   // address of tile row 0 (rows below lo are never read)
+        uint32_t ksb, vsb;  // token strides in bytes (below 2^24: checked on the host)
+        int lo, hi;         // rows read are clamped to [lo, hi]
+        bool general;       // straddles prefix and suffix
+    };
+    auto plan_tile = [&](int t) __attribute__((always_inline)) {
+        TilePlan d;
+        const int key0 = t * kBN - shift;
+        const bool all_suffix = max(key0, 0) >= P;
+        const bool all_prefix = key0 + kBN <= P;
+        d.general = !(all_suffix || all_prefix);
+        const int64_t kpos = all_suffix ? s_row0 + key0 : p_row0 + (d.general ? 0 : key0);
+        d.kb = uniform64(reinterpret_cast<uintptr_t>(all_suffix ? ks : kp) + 2 * kpos * (all_suffix ? ks_ts : kp_ts));
+        d.vb = uniform64(reinterpret_cast<uintptr_t>(all_suffix ? vs : vp) + 2 * kpos * (all_suffix ? vs_ts : vp_ts));
+        d.ksb = 2u * (uint32_t)(all_suffix ? ks_ts : kp_ts);
+        d.vsb = 2u * (uint32_t)(all_suffix ? vs_ts : vp_ts);
+        d.lo = d.general ? 0 : max(-key0, 0);
+        d.hi = d.general ? 0 : kBN - 1;
+        return d;
+    };
+    // Job J of a tile's fast copy: even J = K load of op J/2 (and both
+    // offsets), odd J = V load of that op.
+    auto dma_job = [&](const TilePlan& d, auto SLOT, auto J, uint32_t (&voff)[kOpsPerWave])
+        __attribute__((always_inline)) {
+        constexpr int i = decltype(J)::value / 2;
+        const int row0 = (wave * kOpsPerWave + i) * kRowsPerOp;
+        if constexpr (decltype(J)::value % 2 == 0) {
+            const uint32_t r = (uint32_t)min(max(r_lane[i], d.lo), d.hi);
+            const uint32_t koff = __umul24(r, d.ksb) + kch[i];
+            voff[i] = __umul24(r, d.vsb) + vch;
+            lds_copy16_s(d.kb, koff, d.general ? lds_scratch : kbuf(SLOT) + row0 * D);
         } else {
+            lds_copy16_s(d.vb, voff[i], d.general ? lds_scratch : vbuf(SLOT) + row0 * D);
+        }
+    };
+    // Whole-tile copy issued at once (prologue).
+    auto dma_tile_now = [&](int t, auto SLOT) __attribute__((always_inline)) {
+        const TilePlan d = plan_tile(t);
+        if (d.general) {
 #pragma unroll
             for (int i = 0; i < kOpsPerWave; ++i) dma_op(t, SLOT, i);
         }
+        uint32_t voff[kOpsPerWave];
+        static_for<2 * kOpsPerWave>([&](auto J) __attribute__((always_inline)) { dma_job(d, SLOT, J, voff); });
     };
 
     // ---- per-lane LDS fragment addresses (loop invariant; the tile slot and
@@ -425,7 +476,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     bf16x8_t kpre[2];
     auto unit = [&](auto KSN, auto KBN, auto VS, auto KBC, auto KSNN, auto KBNN,
                     f32x16_t (&sc)[kQB], f32x16_t (&sn)[kQB], const bf16x8_t (&pc0)[2],
-                    bf16x8_t (&pn0)[2], bool valid_next, auto MASK_NEXT) __attribute__((always_inline)) {
+                    bf16x8_t (&pn0)[2], bool valid_next, auto MASK_NEXT, auto&& jobs) __attribute__((always_inline)) {
         bf16x8_t kf[kDS];
         kf[0] = kpre[0];
         kf[1] = kpre[1];
@@ -443,6 +494,8 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
             });
             if constexpr (i == kXSlots - 4) vf[0] = read_v(VS, KBC, 0, 0);
             if constexpr (i == kXSlots - 2) vf[1] = read_v(VS, KBC, 0, 1);
+            // next-tile copy jobs in the odd slots (those read no K fragment)
+            if constexpr (i % 2 == 1) jobs(ic<i / 2>{});
             __builtin_amdgcn_sched_barrier(0);
         });
         w_tail(w1);
@@ -474,9 +527,9 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     //      query block's weights of unit (0, 0).
     f32x16_t sA[kQB], sB[kQB];
     bf16x8_t pA0[2], pB0[2];
-    dma_tile(0, ic<0>{});
-    dma_tile(min(1, ntiles - 1), ic<1>{});
-    dma_tile(min(2, ntiles - 1), ic<2>{});
+    dma_tile_now(0, ic<0>{});
+    dma_tile_now(min(1, ntiles - 1), ic<1>{});
+    dma_tile_now(min(2, ntiles - 1), ic<2>{});
     // tiles 0 and 1 must have landed; tile 2 may still be in flight
     tile_barrier();
 #pragma unroll
@@ -506,10 +559,19 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     auto body = [&](int t, auto S, auto FIRST) __attribute__((always_inline)) {
         constexpr int s = decltype(S)::value;
         constexpr int s1 = (s + 1) % 4, s3 = (s + 3) % 4;
-        dma_tile(min(t + 3, ntiles - 1), ic<s3>{});
-        unit(ic<s>{}, ic<1>{}, ic<s>{}, ic<0>{}, ic<s1>{}, ic<0>{}, sA, sB, pA0, pB0, true, FIRST);
+        const int tt = min(t + 3, ntiles - 1);
+        const TilePlan d = plan_tile(tt);
+        if (d.general) {
+#pragma unroll
+            for (int i = 0; i < kOpsPerWave; ++i) dma_op(tt, ic<s3>{}, i);
+        }
+        uint32_t voff[kOpsPerWave];
+        auto copy_jobs = [&](auto J) __attribute__((always_inline)) { dma_job(d, ic<s3>{}, J, voff); };
+        auto no_jobs = [&](auto J) __attribute__((always_inline)) {};
+        unit(ic<s>{}, ic<1>{}, ic<s>{}, ic<0>{}, ic<s1>{}, ic<0>{}, sA, sB, pA0, pB0, true, FIRST,
+             copy_jobs);
         unit(ic<s1>{}, ic<0>{}, ic<s>{}, ic<1>{}, ic<s1>{}, ic<1>{}, sB, sA, pB0, pA0,
-             t + 1 < ntiles, std::false_type{});
+             t + 1 < ntiles, std::false_type{}, no_jobs);
         // Tiles up to t+2 must have landed before the barrier (tile t+2 is
         // first read in the next tile); this tile's own prefetch (t+3, the
         // last kOpsPerWave*2 loads) may stay in flight.

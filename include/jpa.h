@@ -78,7 +78,8 @@ typedef enum jpa_dtype {
  * as a token-strided slice of a fused QKV projection output (sglang PR
  * #26973 review, Cosmos3 cross-attention snippet).
  * Requirements: data 16-byte aligned; token_stride and head_stride multiples
- * of 8; head_stride >= head_dim; token_stride >= heads * head_stride.
+ * of 8; head_stride >= head_dim; token_stride >= heads * head_stride; for the
+ * four K/V tensors token_stride < 2^23 (8 Mi elements per token).
  * data may be NULL only when tokens == 0.
  */
 typedef struct jpa_tensor {

@@ -196,6 +196,28 @@ def test_null_pointers_and_bad_counts_from_c():
     assert lib.jpa_plan(2, P(cq), P(cp), P(bad), 4, 64, None, None) == jpa.JPA_ERR_SEGMENTS
 
 
+def test_kv_token_stride_limit():
+    # K/V rows are addressed with a 24-bit multiply of the byte stride: token
+    # strides of 2^23 elements or more are rejected (only for K/V tensors).
+    lib = jpa.load_library()
+    kw = _valid_call()
+    d = [jpa.descriptor(kw[n]) for n in ("q", "k_prefix", "v_prefix", "k_suffix", "v_suffix")]
+    od = jpa.descriptor(kw["out"])
+    cq, cp, cs = (np.asarray(kw[n], np.int32) for n in ("cu_q", "cu_prefix", "cu_suffix_real"))
+    P = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def check(which, stride):
+        dd = [jpa.descriptor(kw[n]) for n in ("q", "k_prefix", "v_prefix", "k_suffix", "v_suffix")]
+        dd[which].token_stride = stride
+        return lib.jpa_validate(*[ctypes.byref(x) for x in dd], 2, P(cq), P(cp), P(cs), 0.1,
+                                ctypes.byref(od), None)
+
+    for which in (1, 2, 3, 4):
+        assert check(which, (1 << 23) - 8) == jpa.JPA_OK
+        assert check(which, 1 << 23) == jpa.JPA_ERR_LAYOUT
+    assert check(0, 1 << 23) == jpa.JPA_OK       # queries are not limited
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a GPU")
 def test_forward_without_gpu_reports_hip_error():
     kw = _valid_call()
