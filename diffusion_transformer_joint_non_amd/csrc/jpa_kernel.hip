@@ -30,11 +30,13 @@
 //   unit u+1 are issued alongside the weights of unit u (second query
 //   block), and the PV MFMAs of unit u alongside the first query block's
 //   weights of unit u+1, one score register per MFMA slot.
-// * The key loop walks one index space [0, P_b + R_b): a key below P_b is
-//   read from the prefix tensor, the rest from the suffix tensor, per row,
-//   so the two tensors are never concatenated.  The tile grid is shifted so
-//   it ends exactly at P_b + R_b: only the first tile is partial (its head
-//   is masked) and no pad slot is ever loaded.
+// * Keys are walked in 64-key tiles drawn from both tensors, per row, so the
+//   two tensors are never concatenated and no pad slot is ever loaded.  The
+//   order of keys is free (the attention is non-causal): the P_b mod 64
+//   first prefix keys and the R_b mod 64 last real suffix keys go first, in
+//   one or two mixed tiles (only the first one partial, its tail masked),
+//   then every full 64-key tile of the prefix, then of the suffix.  So every
+//   tile inside the loop is a full run of 64 consecutive rows of one tensor.
 // * Online softmax in the log2 domain, fp32, with a lazy rescale: weights
 //   are formed against a running reference without computing the unit's max;
 //   only when a lane's partial sum exceeds 2^8 does the wave move the
@@ -119,10 +121,16 @@ __device__ __forceinline__ void lds_copy16(const void* gaddr, const void* lds_ds
     asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(gaddr), "{m0}"(m0v) : "memory");
 }
 
-// Same copy from a wave-uniform base address plus a 32-bit per-lane offset.
-__device__ __forceinline__ void lds_copy16_s(uintptr_t sbase, uint32_t voff, const void* lds_dst) {
+// Buffer resource for raw 16-byte loads: base address, no stride, num_records
+// bytes in range (lanes at or past it read nothing and write zeros to LDS).
+__device__ __forceinline__ u32x4_t make_rsrc(uintptr_t base, uint32_t num_records) {
+    return u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, num_records, 0x00020000u};
+}
+// 16-byte-per-lane buffer -> LDS copy (buffer_load_dwordx4 ... lds) at a
+// 32-bit per-lane offset; untracked like lds_copy16.
+__device__ __forceinline__ void lds_copy16_buf(u32x4_t rsrc, uint32_t voff, const void* lds_dst) {
     const uint32_t m0v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst;
-    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(m0v) : "memory");
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(voff), "s"(rsrc), "{m0}"(m0v) : "memory");
 }
 
 // A wave-uniform 64-bit value in scalar registers.
@@ -224,17 +232,23 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     const uint16_t* const vp = p.vp + (int64_t)hk * p.vp_hs;
     const uint16_t* const ks = p.ks + (int64_t)hk * p.ks_hs;
     const uint16_t* const vs = p.vs + (int64_t)hk * p.vs_hs;
-    // key k < P is prefix token p_row0 + k; key k >= P is suffix slot s_row0 + k
-    const int64_t p_row0 = p.rows[b].p_start;
-    const int64_t s_row0 = (int64_t)p.rows[b].s_start - P;
+    const int R = Nk - P;
+    const int64_t p_row0 = p.rows[b].p_start;      // prefix token of prefix key 0
+    const int64_t s_row0 = p.rows[b].s_start;      // suffix slot of suffix key 0
     // Token strides as scalars: a per-lane choice between them must select
     // registers, never re-read the kernel arguments per lane.
     int64_t kp_ts = p.kp_ts, ks_ts = p.ks_ts, vp_ts = p.vp_ts, vs_ts = p.vs_ts;
     asm("" : "+s"(kp_ts), "+s"(ks_ts), "+s"(vp_ts), "+s"(vs_ts));
-    // The key walk is shifted so that the tiles end exactly at Nk: only tile
-    // 0 can be partial, and its missing keys are the negative indices.
-    const int ntiles = (Nk + kBN - 1) / kBN;
-    const int shift = ntiles * kBN - Nk;
+    // Tile order: npart mixed tiles holding the headP = P mod 64 first prefix
+    // keys and the tailR = R mod 64 last suffix keys (tile 0 holds n0 of
+    // them, the rest masked; tile 1, if any, is full), then Pf full prefix
+    // tiles (prefix keys headP + 64i ..), then Rf full suffix tiles.
+    const int headP = P & (kBN - 1), Pf = P / kBN;
+    const int tailR = R & (kBN - 1), Rf = R / kBN;
+    const int X = headP + tailR;
+    const int npart = X == 0 ? 0 : (X <= kBN ? 1 : 2);
+    const int n0 = npart == 0 ? kBN : (npart == 1 ? X : X - kBN);
+    const int ntiles = npart + Pf + Rf;
 
     // ---- Q fragments (B operand of S^T = K Q^T): lane (j, h) holds
     //      q[row j][16*ds + 8*h .. +7] for every k-step ds.  Rows past the
@@ -256,33 +270,32 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         for (int ds = 0; ds < kDS; ++ds) asm("" : "+a"(qf[qb][ds]));
 
     // ---- global -> LDS tile loads, 16 bytes per lane straight into LDS
-    //      (global_load_lds_dwordx4: lane l of a wave lands at base + 16*l).
-    //      A wave instruction (an "op") fills kRowsPerOp consecutive key rows
-    //      of the tile; each lane fetches the global chunk that belongs at its
-    //      physical LDS slot, which realises the XOR swizzles.  No pad slot is
-    //      ever touched.
-    //  Common case, every key of the tile in one tensor: a scalar tile base
-    //  per tensor plus a 32-bit per-lane offset whose row is clamped to the
-    //  tile's valid rows (the head of tile 0 re-reads its first real key;
-    //  those scores are masked).  Three VALU instructions per K/V pair of
-    //  loads, issued from the MFMA slots of the tile before.
-    //  The one tile per batch row that straddles prefix and suffix is copied
-    //  by a general per-lane path before its unit; its slot loads then re-read
-    //  a valid row into a scratch LDS line that nothing reads.
-    __shared__ __attribute__((aligned(16))) uint16_t lds_scratch[512];
+    //      (lane l of a wave lands at base + 16*l).  A wave instruction (an
+    //      "op") fills kRowsPerOp consecutive key rows of the tile; each lane
+    //      fetches the global chunk that belongs at its physical LDS slot,
+    //      which realises the XOR swizzles.
+    //  Mixed tiles (tile 0, maybe tile 1: loaded before the loop): each lane
+    //  forms its own row address.  Rows of tile 0 past n0 re-read the first
+    //  mixed key; their scores are masked.
     auto dma_op = [&](int t, auto SLOT, int i) __attribute__((always_inline)) {
         const int row0 = (wave * kOpsPerWave + i) * kRowsPerOp;
         const int row = row0 + lane / kCH;
         const int pc = lane % kCH;
-        const int key = max(t * kBN - shift + row, 0);
-        const bool pre = key < P;
-        const uint16_t* gk = (pre ? kp + (p_row0 + key) * kp_ts : ks + (s_row0 + key) * ks_ts) +
-                             ((pc ^ swz_k(row)) & (kCH - 1)) * 8;
-        const uint16_t* gv = (pre ? vp + (p_row0 + key) * vp_ts : vs + (s_row0 + key) * vs_ts) +
-                             ((pc ^ (2 * (row & 3))) & (kCH - 1)) * 8;
-        lds_copy16(gk, kbuf(SLOT) + row0 * D);
-        lds_copy16(gv, vbuf(SLOT) + row0 * D);
+        int pi = t == 0 ? row : n0 + row;            // index among the mixed keys
+        pi = (t == 0 && row >= n0) ? 0 : pi;
+        const bool pre = pi < headP;
+        const int64_t tp = p_row0 + pi;
+        const int64_t ts = s_row0 + (int64_t)Rf * kBN + (pi - headP);
+        const uint16_t* gk = pre ? kp + tp * kp_ts : ks + ts * ks_ts;
+        const uint16_t* gv = pre ? vp + tp * vp_ts : vs + ts * vs_ts;
+        lds_copy16(gk + ((pc ^ swz_k(row)) & (kCH - 1)) * 8, kbuf(SLOT) + row0 * D);
+        lds_copy16(gv + ((pc ^ (2 * (row & 3))) & (kCH - 1)) * 8, vbuf(SLOT) + row0 * D);
     };
+    //  Full tiles: a buffer resource whose base is the tile's row 0 plus a
+    //  32-bit per-lane offset (row * token stride + chunk), fixed per tensor.
+    //  The loop advances the base by 64 rows per tile and switches tensor once;
+    //  its look-ahead past the last tile uses an empty resource (every lane
+    //  out of range: nothing is read, zeros land in a buffer nobody reads).
     const int lane_row = lane / kCH;
     const int lane_pc = lane % kCH;
     int r_lane[kOpsPerWave];            // tile row of this lane in op i
@@ -295,51 +308,61 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     // V chunk: op rows start at multiples of 4, so row & 3 == lane_row & 3
     const uint32_t vch = (uint32_t)((lane_pc ^ (2 * (lane_row & 3))) & (kCH - 1)) << 4;
 
-    struct TilePlan {
-        uintptr_t kb, vb;   // address of tile row 0 (rows below lo are never read)
-        uint32_t ksb, vsb;  // token strides in bytes (below 2^24: checked on the host)
-        int lo, hi;         // rows read are clamped to [lo, hi]
-        bool general;       // straddles prefix and suffix
+    u32x4_t rsk = {0u, 0u, 0u, 0x00020000u};   // K and V resources of the current full tile
+    u32x4_t rsv = rsk;
+    uint32_t step_k = 0, step_v = 0;          // 64 rows of the current tensor, bytes
+    uint32_t koff[kOpsPerWave], voff[kOpsPerWave];
+#pragma unroll
+    for (int i = 0; i < kOpsPerWave; ++i) koff[i] = voff[i] = 0;
+    auto uniform_rsrc = [&](u32x4_t r) __attribute__((always_inline)) {
+        return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane(r[0]), (uint32_t)__builtin_amdgcn_readfirstlane(r[1]),
+                       (uint32_t)__builtin_amdgcn_readfirstlane(r[2]), 0x00020000u};
     };
-    auto plan_tile = [&](int t) __attribute__((always_inline)) {
-        TilePlan d;
-        const int key0 = t * kBN - shift;
-        const bool all_suffix = max(key0, 0) >= P;
-        const bool all_prefix = key0 + kBN <= P;
-        d.general = !(all_suffix || all_prefix);
-        const int64_t kpos = all_suffix ? s_row0 + key0 : p_row0 + (d.general ? 0 : key0);
-        d.kb = uniform64(reinterpret_cast<uintptr_t>(all_suffix ? ks : kp) + 2 * kpos * (all_suffix ? ks_ts : kp_ts));
-        d.vb = uniform64(reinterpret_cast<uintptr_t>(all_suffix ? vs : vp) + 2 * kpos * (all_suffix ? vs_ts : vp_ts));
-        d.ksb = 2u * (uint32_t)(all_suffix ? ks_ts : kp_ts);
-        d.vsb = 2u * (uint32_t)(all_suffix ? vs_ts : vp_ts);
-        d.lo = d.general ? 0 : max(-key0, 0);
-        d.hi = d.general ? 0 : kBN - 1;
-        return d;
+    // Point the copy state at full tile t (npart <= t < ntiles).
+    auto set_full_tile = [&](int t) __attribute__((always_inline)) {
+        const bool suf = t >= npart + Pf;
+        const int64_t tp = p_row0 + headP + (int64_t)(t - npart) * kBN;
+        const int64_t tsf = s_row0 + (int64_t)(t - npart - Pf) * kBN;
+        const uintptr_t kb_p = reinterpret_cast<uintptr_t>(kp) + 2 * tp * kp_ts;
+        const uintptr_t kb_s = reinterpret_cast<uintptr_t>(ks) + 2 * tsf * ks_ts;
+        const uintptr_t vb_p = reinterpret_cast<uintptr_t>(vp) + 2 * tp * vp_ts;
+        const uintptr_t vb_s = reinterpret_cast<uintptr_t>(vs) + 2 * tsf * vs_ts;
+        const uint32_t ksb = 2u * (uint32_t)(suf ? ks_ts : kp_ts);
+        const uint32_t vsb = 2u * (uint32_t)(suf ? vs_ts : vp_ts);
+        rsk = uniform_rsrc(make_rsrc(suf ? kb_s : kb_p, ~0u));
+        rsv = uniform_rsrc(make_rsrc(suf ? vb_s : vb_p, ~0u));
+        step_k = __builtin_amdgcn_readfirstlane(ksb * (uint32_t)kBN);
+        step_v = __builtin_amdgcn_readfirstlane(vsb * (uint32_t)kBN);
+#pragma unroll
+        for (int i = 0; i < kOpsPerWave; ++i) {
+            koff[i] = __umul24((uint32_t)r_lane[i], ksb) + kch[i];
+            voff[i] = __umul24((uint32_t)r_lane[i], vsb) + vch;
+        }
     };
-    // Job J of a tile's fast copy: even J = K load of op J/2 (and both
-    // offsets), odd J = V load of that op.
-    auto dma_job = [&](const TilePlan& d, auto SLOT, auto J, uint32_t (&voff)[kOpsPerWave])
-        __attribute__((always_inline)) {
+    // Next full tile of the same tensor: base + 64 rows (the base stays below
+    // 2^48, so word 1 holds only address bits and no carry leaves it).
+    auto advance = [&](u32x4_t& r, uint32_t step) __attribute__((always_inline)) {
+        const uint64_t b = ((uint64_t)r[1] << 32 | r[0]) + step;
+        r = uniform_rsrc(u32x4_t{(uint32_t)b, (uint32_t)(b >> 32), r[2], 0x00020000u});
+    };
+    // Job J of the copy of the current full tile: even J = K of op J/2, odd = V.
+    auto fast_job = [&](auto SLOT, auto J) __attribute__((always_inline)) {
         constexpr int i = decltype(J)::value / 2;
         const int row0 = (wave * kOpsPerWave + i) * kRowsPerOp;
-        if constexpr (decltype(J)::value % 2 == 0) {
-            const uint32_t r = (uint32_t)min(max(r_lane[i], d.lo), d.hi);
-            const uint32_t koff = __umul24(r, d.ksb) + kch[i];
-            voff[i] = __umul24(r, d.vsb) + vch;
-            lds_copy16_s(d.kb, koff, d.general ? lds_scratch : kbuf(SLOT) + row0 * D);
-        } else {
-            lds_copy16_s(d.vb, voff[i], d.general ? lds_scratch : vbuf(SLOT) + row0 * D);
-        }
+        if constexpr (decltype(J)::value % 2 == 0)
+            lds_copy16_buf(rsk, koff[i], kbuf(SLOT) + row0 * D);
+        else
+            lds_copy16_buf(rsv, voff[i], vbuf(SLOT) + row0 * D);
     };
-    // Whole-tile copy issued at once (prologue).
+    // Whole-tile copy issued at once (before the loop).
     auto dma_tile_now = [&](int t, auto SLOT) __attribute__((always_inline)) {
-        const TilePlan d = plan_tile(t);
-        if (d.general) {
+        if (t < npart) {
 #pragma unroll
             for (int i = 0; i < kOpsPerWave; ++i) dma_op(t, SLOT, i);
+        } else {
+            set_full_tile(t);
+            static_for<2 * kOpsPerWave>([&](auto J) __attribute__((always_inline)) { fast_job(SLOT, J); });
         }
-        uint32_t voff[kOpsPerWave];
-        static_for<2 * kOpsPerWave>([&](auto J) __attribute__((always_inline)) { dma_job(d, SLOT, J, voff); });
     };
 
     // ---- per-lane LDS fragment addresses (loop invariant; the tile slot and
@@ -390,12 +413,12 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     }
     const float c = p.c;
 
-    // Scores of negative keys (head of tile 0) -> -FLT_MAX.  A finite value
-    // keeps a fully masked unit NaN-free: its weights underflow to 0.
+    // Scores of the unused rows of tile 0 (at or past n0) -> -FLT_MAX.  A
+    // finite value keeps a fully masked unit NaN-free: its weights are 0.
     auto mask_head = [&](f32x16_t (&s)[kQB], int kb) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const bool dead = kb * 32 + perm_k(8 * (r >> 2) + 4 * h + (r & 3)) < shift;
+            const bool dead = kb * 32 + perm_k(8 * (r >> 2) + 4 * h + (r & 3)) >= n0;
 #pragma unroll
             for (int qb = 0; qb < kQB; ++qb) s[qb][r] = dead ? -3.402823466e38f : s[qb][r];
         }
@@ -559,14 +582,19 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     auto body = [&](int t, auto S, auto FIRST) __attribute__((always_inline)) {
         constexpr int s = decltype(S)::value;
         constexpr int s1 = (s + 1) % 4, s3 = (s + 3) % 4;
-        const int tt = min(t + 3, ntiles - 1);
-        const TilePlan d = plan_tile(tt);
-        if (d.general) {
-#pragma unroll
-            for (int i = 0; i < kOpsPerWave; ++i) dma_op(tt, ic<s3>{}, i);
+        // Copy state for tile t+3 (always a full tile): advance 64 rows, or
+        // switch to the suffix, or an empty resource past the last tile.
+        const int tt = t + 3;
+        if (tt >= ntiles) {
+            rsk[2] = 0u;
+            rsv[2] = 0u;
+        } else if (tt == npart + Pf) {
+            set_full_tile(tt);
+        } else {
+            advance(rsk, step_k);
+            advance(rsv, step_v);
         }
-        uint32_t voff[kOpsPerWave];
-        auto copy_jobs = [&](auto J) __attribute__((always_inline)) { dma_job(d, ic<s3>{}, J, voff); };
+        auto copy_jobs = [&](auto J) __attribute__((always_inline)) { fast_job(ic<s3>{}, J); };
         auto no_jobs = [&](auto J) __attribute__((always_inline)) {};
         unit(ic<s>{}, ic<1>{}, ic<s>{}, ic<0>{}, ic<s1>{}, ic<0>{}, sA, sB, pA0, pB0, true, FIRST,
              copy_jobs);

@@ -111,10 +111,14 @@ def test_pad_contents_are_never_read(case):
         assert np.array_equal(res[0][1].view(np.int32), b[1].view(np.int32))
 
 
-def test_split_equals_concat_bitwise():
-    """Same keys given as prefix+suffix or as one suffix: the key walk visits
-    the same tiles in the same order, so the result is bitwise identical
-    (sglang PR #26973 review: non-SP branches concatenate then attend)."""
+def test_split_equals_concat():
+    """Same keys given as prefix+suffix or as one suffix give the same
+    attention (sglang PR #26973 review: non-SP branches concatenate then
+    attend).  The kernel's key order depends on how the keys are split (the
+    partial 64-key runs of each tensor go first), so the two runs differ only
+    by rounding (accumulation order and the bf16 rounding of weights taken
+    against a different running reference): both meet the oracle bar, and
+    they agree within 4e-3 max / 5e-5 mean on outputs and 1e-5 on the LSE."""
     w = synth.custom_workload(4, 4, 128, [77, 512], [819, 190], [2, 70], "prefix+suffix", wid=610)
     x = synth.make_inputs(w, pad_fill="garbage")
     o1, l1 = gh.run(x)
@@ -132,8 +136,17 @@ def test_split_equals_concat_bitwise():
               v_suffix=np.concatenate(vs), cu_prefix=np.zeros(w.batch + 1, np.int32),
               cu_suffix_real=np.asarray(cs, np.int32))
     o2, l2 = gh.run(x2)
-    assert np.array_equal(gh.bits(o1), gh.bits(o2))
-    assert torch.equal(l1, l2)
+    for o, l in ((o1, l1), (o2, l2)):
+        oh, lh = gh.host(o, l)
+        gh.assert_parity_full(w, x, oh, lh)
+    a, b = o1.float().cpu(), o2.float().cpu()
+    real = torch.from_numpy(~w.pad_query_mask())
+    d = (a[real] - b[real]).abs()
+    assert float(d.max()) <= 4e-3 and float(d.mean()) <= 5e-5, (float(d.max()), float(d.mean()))
+    assert torch.equal(a[~real], b[~real])
+    la, lb = l1.cpu()[:, real], l2.cpu()[:, real]
+    assert float((la - lb).abs().max()) <= 1e-5
+    assert torch.equal(l1.cpu()[:, ~real], l2.cpu()[:, ~real])       # pad rows: -inf in both
 
 
 def test_strided_views_match_contiguous():
