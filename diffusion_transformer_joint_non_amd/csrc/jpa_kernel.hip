@@ -155,7 +155,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     constexpr int kOpsPerWave = kBN / kRowsPerOp / kWaves;
     constexpr int kXSlots = kDS * kQB;       // QK MFMAs per 32-key unit
     constexpr int kYSlots = kDB * 2 * kQB;   // PV MFMAs per 32-key unit
-    static_assert(kXSlots / 2 == 2 * kOpsPerWave, "one copy job per odd X slot");
+    static_assert(kYSlots / 2 == 2 * kOpsPerWave, "one copy job per odd Y slot");
 
     // Barrier that lets the most recent tile prefetch (2*kOpsPerWave loads
     // of this wave) stay in flight: s_waitcnt vmcnt(N) lgkmcnt(0); s_barrier.
@@ -391,12 +391,6 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         constexpr int off = decltype(KB)::value * 32 * D;
         return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(kbuf(SLOT) + k_lane[ds] + off));
     };
-    auto read_v = [&](auto SLOT, auto KB, int db, int u) __attribute__((always_inline)) {
-        const uint16_t* a = vbuf(SLOT) + v_lane[db] + (decltype(KB)::value * 32 + 16 * u) * D;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a + 4 * D));
-        return __builtin_bit_cast(bf16x8_t, s16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-    };
 
     f32x16_t o[kQB][kDB];
     float m_ref[kQB], l_sum[kQB];
@@ -493,32 +487,46 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     //  X slots: QK^T MFMAs of the next unit (K tile KSN, half KBN) -> sn, with
     //           the weights of the current unit's second query block.
     //  Y slots: PV MFMAs of the current unit (V tile VS, half KBC), with the
-    //           weights of the next unit's first query block.
-    //  The first two K fragments of every X phase are read at the end of the
-    //  previous Y phase (kpre), the first two V fragments at the end of X.
-    bf16x8_t kpre[2];
+    //           weights of the next unit's first query block, the K reads of
+    //           the next X phase and, in the first unit of a tile, the copy of
+    //           a later tile.
+    // LDS fragments are read one phase ahead: the K fragments of an X phase
+    // during the Y phase before it (kq), the V fragments of a Y phase during
+    // the X phase before it (one transposed read per slot).  Each phase then
+    // waits twice on lgkmcnt (LDS reads complete in order), each time for
+    // reads issued at least half a phase earlier.
+    bf16x8_t kq[kDS];
+    auto lgkm_wait = [&](auto N) __attribute__((always_inline)) {
+        constexpr int n = decltype(N)::value;
+        static_assert(n >= 0 && n < 16, "lgkmcnt field is 4 bits");
+        __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (n << 8) | (3 << 14));
+    };
+    auto read_v_half = [&](auto SLOT, auto KB, int f, int half) __attribute__((always_inline)) {
+        const int db = f / 2, u = f % 2;
+        const uint16_t* a = vbuf(SLOT) + v_lane[db] + (decltype(KB)::value * 32 + 16 * u) * D + half * 4 * D;
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a));
+    };
     auto unit = [&](auto KSN, auto KBN, auto VS, auto KBC, auto KSNN, auto KBNN,
                     f32x16_t (&sc)[kQB], f32x16_t (&sn)[kQB], const bf16x8_t (&pc0)[2],
                     bf16x8_t (&pn0)[2], bool valid_next, auto MASK_NEXT, auto&& jobs) __attribute__((always_inline)) {
-        bf16x8_t kf[kDS];
-        kf[0] = kpre[0];
-        kf[1] = kpre[1];
-        bf16x8_t vf[kDB * 2];
+        constexpr int kVF = kDB * 2;                 // V fragments per unit (two reads each)
+        static_assert(2 * kVF == kXSlots, "one transposed V read per X slot");
+        static_assert(kYSlots == 2 * kDS, "one K read per two Y slots");
+        s16x4_t vlo[kVF], vhi[kVF];
         Weights w1;
         // X phase
         static_for<kXSlots>([&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
             constexpr int ds = i / kQB, qb = i % kQB;
-            if constexpr (qb == 0 && ds + 2 < kDS) kf[ds + 2] = read_k(KSN, KBN, ds + 2);
-            sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[qb][ds],
+            if constexpr (i == 0) lgkm_wait(ic<kDS / 2>{});            // kq[0, kDS/2)
+            if constexpr (i == kXSlots / 2) lgkm_wait(ic<kXSlots / 2>{});  // rest of kq
+            sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[ds], qf[qb][ds],
                                                              ds == 0 ? f32x16_t{} : sn[qb], 0, 0, 0);
             static_for<16>([&](auto R) __attribute__((always_inline)) {
                 if constexpr (decltype(R)::value * kXSlots / 16 == i) w_step(sc[1], m_ref[1], w1, R);
             });
-            if constexpr (i == kXSlots - 4) vf[0] = read_v(VS, KBC, 0, 0);
-            if constexpr (i == kXSlots - 2) vf[1] = read_v(VS, KBC, 0, 1);
-            // next-tile copy jobs in the odd slots (those read no K fragment)
-            if constexpr (i % 2 == 1) jobs(ic<i / 2>{});
+            if constexpr (i % 2 == 0) vlo[i / 2] = read_v_half(VS, KBC, i / 2, 0);
+            else vhi[i / 2] = read_v_half(VS, KBC, i / 2, 1);
             __builtin_amdgcn_sched_barrier(0);
         });
         w_tail(w1);
@@ -529,16 +537,20 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         Weights w0;
         static_for<kYSlots>([&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
-            constexpr int step = i / kQB, qb = i % kQB;     // step = (db, u)
+            constexpr int step = i / kQB, qb = i % kQB;     // step = (db, u) = V fragment
             constexpr int db = step / 2, u = step % 2;
-            if constexpr (qb == 0 && step + 2 < kDB * 2) vf[step + 2] = read_v(VS, KBC, (step + 2) / 2, (step + 2) % 2);
-            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[step], qb == 0 ? pc0[u] : p1[u], o[qb][db], 0, 0, 0);
+            if constexpr (i == 0) lgkm_wait(ic<kXSlots / 2>{});            // V fragments [0, kVF/2)
+            if constexpr (i == kYSlots / 2) lgkm_wait(ic<kDS / 2>{});      // the rest of V
+            const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, s16x8_t{
+                vlo[step][0], vlo[step][1], vlo[step][2], vlo[step][3],
+                vhi[step][0], vhi[step][1], vhi[step][2], vhi[step][3]});
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, qb == 0 ? pc0[u] : p1[u], o[qb][db], 0, 0, 0);
             if constexpr (i == 0 && decltype(MASK_NEXT)::value) mask_head(sn, decltype(KBN)::value);
             static_for<16>([&](auto R) __attribute__((always_inline)) {
                 if constexpr (decltype(R)::value * kYSlots / 16 == i) w_step(sn[0], m_ref[0], w0, R);
             });
-            if constexpr (i == kYSlots - 3) kpre[0] = read_k(KSNN, KBNN, 0);
-            if constexpr (i == kYSlots - 1) kpre[1] = read_k(KSNN, KBNN, 1);
+            if constexpr (i % 2 == 0) kq[i / 2] = read_k(KSNN, KBNN, i / 2);
+            else jobs(ic<i / 2>{});                  // next-tile copy (first unit of a tile)
             __builtin_amdgcn_sched_barrier(0);
         });
         w_tail(w0);
@@ -571,8 +583,8 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         pack_frags(w0.pk, pA0);
         l_sum[0] = w0.part;
     }
-    kpre[0] = read_k(ic<0>{}, ic<1>{}, 0);
-    kpre[1] = read_k(ic<0>{}, ic<1>{}, 1);
+#pragma unroll
+    for (int ds = 0; ds < kDS; ++ds) kq[ds] = read_k(ic<0>{}, ic<1>{}, ds);
 
     // ---- one 64-key tile in buffer S (of 4): units (t,0) and (t,1); tile t+3
     //      is fetched into buffer S+3 meanwhile (clamped to the last tile, so
