@@ -5,6 +5,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <vector>
+#include <algorithm>
 
 #include "jpa.h"
 #include "jpa_params.h"
@@ -96,6 +98,54 @@ jpa_status validate(const jpa_tensor* q, const jpa_tensor* k_prefix, const jpa_t
     return JPA_OK;
 }
 
+// Compute units of the current device.
+jpa_status device_cus(int* cus) {
+    *cus = jpa_device_cus();
+    return *cus > 0 ? JPA_OK : JPA_ERR_HIP;
+}
+
+// Work split of one launch over `wgs` compute units (0: one workgroup per
+// item).  Items are (query head, query tile); a real item weighs its key
+// tiles, an all-pad item 1.  Whole rounds of wgs items run one item per
+// workgroup; the items of the last, partial round are cut into wgs balanced
+// ranges of key tiles, whose cut items a second kernel merges.
+void plan_split(jpa_kernel_params& p, int wgs, bool forced, char* ws, int head_dim) {
+    const int64_t items = (int64_t)p.total_tiles * p.hq;
+    int64_t head_units = 0;
+    std::vector<int64_t> tile_units(p.total_tiles);
+    for (int b = 0; b < p.nrows; ++b) {
+        const jpa_kernel_row& r = p.rows[b];
+        const int nt = (r.q_slots + JPA_BLOCK_M - 1) / JPA_BLOCK_M;
+        const int nr = (r.q_real + JPA_BLOCK_M - 1) / JPA_BLOCK_M;
+        const int nk = (r.keys + 63) / 64;
+        for (int t = 0; t < nt; ++t) tile_units[r.tile_start + t] = t < nr ? nk : 1;
+        head_units += (int64_t)nr * nk + (nt - nr);
+    }
+    p.head_units = head_units;
+    p.n_dp = (int32_t)items;
+    p.sk_wgs = 0;
+    p.tail_unit0 = p.tail_units = 0;
+    p.ws_o = nullptr;
+    p.ws_lse = nullptr;
+    if (wgs <= 0 || items % wgs == 0) return;
+    // Unless asked for, split only when the last round would leave more than
+    // half of the units idle: cut pieces each pay a prologue and a merge, so a
+    // nearly full last round is faster uncut.
+    if (!forced && 2 * (items % wgs) > wgs) return;
+    const int64_t n_dp = items / wgs * wgs;
+    int64_t unit0 = 0, tail = 0;
+    for (int64_t it = 0; it < items; ++it) {
+        const int64_t u = tile_units[it % p.total_tiles];
+        if (it < n_dp) unit0 += u; else tail += u;
+    }
+    p.n_dp = (int32_t)n_dp;
+    p.sk_wgs = (int32_t)std::min<int64_t>(wgs, tail);
+    p.tail_unit0 = unit0;
+    p.tail_units = tail;
+    p.ws_o = reinterpret_cast<float*>(ws);
+    p.ws_lse = reinterpret_cast<float*>(ws + jpa_ws_o_bytes(wgs, head_dim));
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,14 +175,41 @@ JPA_API jpa_status jpa_plan(int32_t batch, const int32_t* cu_q, const int32_t* c
     return JPA_OK;
 }
 
+JPA_API size_t jpa_workspace_bytes(int32_t head_dim, int32_t split_wgs) {
+    if (head_dim != 64 && head_dim != 128) return 0;
+    int wgs = split_wgs;
+    if (wgs <= 0 && device_cus(&wgs) != JPA_OK) return 0;
+    return jpa_ws_o_bytes(wgs, head_dim) + jpa_ws_lse_bytes(wgs);
+}
+
 JPA_API jpa_status jpa_forward(const jpa_tensor* q, const jpa_tensor* k_prefix,
                                const jpa_tensor* v_prefix, const jpa_tensor* k_suffix,
                                const jpa_tensor* v_suffix, int32_t batch, const int32_t* cu_q,
                                const int32_t* cu_prefix, const int32_t* cu_suffix_real,
                                float scale, const jpa_tensor* out, float* lse, void* stream) {
+    return jpa_forward_ws(q, k_prefix, v_prefix, k_suffix, v_suffix, batch, cu_q, cu_prefix,
+                          cu_suffix_real, scale, out, lse, nullptr, 0, 0, stream);
+}
+
+JPA_API jpa_status jpa_forward_ws(const jpa_tensor* q, const jpa_tensor* k_prefix,
+                                  const jpa_tensor* v_prefix, const jpa_tensor* k_suffix,
+                                  const jpa_tensor* v_suffix, int32_t batch, const int32_t* cu_q,
+                                  const int32_t* cu_prefix, const int32_t* cu_suffix_real,
+                                  float scale, const jpa_tensor* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, int32_t split_wgs,
+                                  void* stream) {
     jpa_status st = validate(q, k_prefix, v_prefix, k_suffix, v_suffix, batch, cu_q, cu_prefix,
                              cu_suffix_real, scale, out, lse);
     if (st != JPA_OK) return st;
+    int wgs = 0;
+    if (workspace) {
+        if (split_wgs < 0) return JPA_ERR_VALUE;
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u) return JPA_ERR_LAYOUT;
+        wgs = split_wgs;
+        if (wgs == 0 && device_cus(&wgs) != JPA_OK) return JPA_ERR_HIP;
+        if (workspace_bytes < jpa_ws_o_bytes(wgs, q->head_dim) + jpa_ws_lse_bytes(wgs))
+            return JPA_ERR_VALUE;
+    }
 
     jpa_kernel_params p;
     std::memset(&p, 0, sizeof(p));
@@ -185,6 +262,7 @@ JPA_API jpa_status jpa_forward(const jpa_tensor* q, const jpa_tensor* k_prefix,
         }
         if (p.nrows == 0) continue;
         if ((int64_t)p.total_tiles * p.hq > INT32_MAX) return JPA_ERR_SHAPE;
+        plan_split(p, wgs, split_wgs > 0, static_cast<char*>(workspace), q->head_dim);
         if (jpa_launch_kernel(p, q->head_dim, stream) != 0) return JPA_ERR_HIP;
     }
     return JPA_OK;

@@ -127,10 +127,15 @@ __device__ __forceinline__ u32x4_t make_rsrc(uintptr_t base, uint32_t num_record
     return u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, num_records, 0x00020000u};
 }
 // 16-byte-per-lane buffer -> LDS copy (buffer_load_dwordx4 ... lds) at a
-// 32-bit per-lane offset; untracked like lds_copy16.
-__device__ __forceinline__ void lds_copy16_buf(u32x4_t rsrc, uint32_t voff, const void* lds_dst) {
-    const uint32_t m0v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst;
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(voff), "s"(rsrc), "{m0}"(m0v) : "memory");
+// 32-bit per-lane offset; untracked like lds_copy16.  The LDS address is
+// lds_base + OFF (bytes), formed in m0 inside the asm so that only lds_base
+// occupies a scalar register.
+template <int OFF>
+__device__ __forceinline__ void lds_copy16_buf(u32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
+    rsrc = u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds_base), "n"(OFF) : "memory", "m0", "scc");
 }
 
 // A wave-uniform 64-bit value in scalar registers.
@@ -169,31 +174,103 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k0[kTile];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k1[kTile];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k2[kTile];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k3[kTile];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v0[kTile];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v1[kTile];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v2[kTile];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v3[kTile];
+    // Four K and four V tile buffers.  The tile copies are untracked inline
+    // asm, so no compiler-inserted wait depends on how they are laid out.
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k[4 * kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[4 * kTile];
     auto kbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint16_t* {
-        constexpr int s = decltype(SLOT)::value;
-        if constexpr (s == 0) return lds_k0; else if constexpr (s == 1) return lds_k1;
-        else if constexpr (s == 2) return lds_k2; else return lds_k3;
+        return lds_k + decltype(SLOT)::value * kTile;
     };
     auto vbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint16_t* {
-        constexpr int s = decltype(SLOT)::value;
-        if constexpr (s == 0) return lds_v0; else if constexpr (s == 1) return lds_v1;
-        else if constexpr (s == 2) return lds_v2; else return lds_v3;
+        return lds_v + decltype(SLOT)::value * kTile;
     };
 
-    // ---- work item: XCD-grouped order over (head, row, query tile)
-    const int nblk = gridDim.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31;                 // query column inside a 32-block
+    const int h = lane >> 5;                 // lane half
+
+    // ---- work split (jpa_kernel_params): per row of the launch, a real query
+    //      tile counts its key tiles as units, an all-pad query tile counts 1.
+    auto row_counts = [&](int rb, int& nt, int& nr, int& nk) __attribute__((always_inline)) {
+        nt = (p.rows[rb].q_slots + kBM - 1) / kBM;
+        nr = (p.rows[rb].q_real + kBM - 1) / kBM;
+        nk = (p.rows[rb].keys + kBN - 1) / kBN;
+    };
+    // absolute unit of the first key tile of item it
+    auto item_unit = [&](int it) __attribute__((always_inline)) -> int64_t {
+        const int hq_ = it / p.total_tiles, tile_ = it - hq_ * p.total_tiles;
+        int64_t acc = (int64_t)hq_ * p.head_units;
+        for (int rb = 0; rb < p.nrows; ++rb) {
+            int nt, nr, nk;
+            row_counts(rb, nt, nr, nk);
+            const int tr = tile_ - p.rows[rb].tile_start;
+            if (tr < nt) {
+                acc += tr < nr ? (int64_t)tr * nk : (int64_t)nr * nk + (tr - nr);
+                break;
+            }
+            acc += (int64_t)nr * nk + (nt - nr);
+        }
+        return acc;
+    };
+    // item and key-tile offset of absolute unit U
+    auto locate = [&](int64_t U, int& it, int& off) __attribute__((always_inline)) {
+        const int hq_ = (int)(U / p.head_units);
+        int64_t r = U - (int64_t)hq_ * p.head_units;
+        it = hq_ * p.total_tiles;
+        off = 0;
+        for (int rb = 0; rb < p.nrows; ++rb) {
+            int nt, nr, nk;
+            row_counts(rb, nt, nr, nk);
+            const int64_t ru = (int64_t)nr * nk + (nt - nr);
+            if (r < ru || rb + 1 == p.nrows) {
+                const int64_t realu = (int64_t)nr * nk;
+                int tr;
+                if (r < realu) {
+                    tr = (int)(r / nk);
+                    off = (int)(r - (int64_t)tr * nk);
+                } else {
+                    tr = nr + (int)(r - realu);
+                }
+                it += p.rows[rb].tile_start + tr;
+                break;
+            }
+            r -= ru;
+        }
+    };
+    // balanced ranges: range w covers tail units [rstart(w), rstart(w + 1))
+    auto rstart = [&](int64_t w) __attribute__((always_inline)) -> int64_t {
+        return w * p.tail_units / p.sk_wgs;
+    };
+    // XCD-grouped order: the workgroups resident on one XCD (blocks are dealt
+    // round-robin over the 8 XCDs) take consecutive items or ranges, which
+    // then stream the same K/V through that XCD's L2.
+    auto xcd_order = [&](int l, int n) __attribute__((always_inline)) {
+        const int x = l & 7, per = n >> 3, rem = n & 7;
+        return x * per + min(x, rem) + (l >> 3);
+    };
+
     const int bid = blockIdx.x;
-    const int xcd = bid & 7;
-    const int per = nblk >> 3, rem = nblk & 7;
-    const int item = xcd * per + min(xcd, rem) + (bid >> 3);
+    const bool dp = bid < p.n_dp;
+    int w_me = 0;
+    int64_t u_next = 0, u_end = 0;
+    if (!dp) {
+        w_me = xcd_order(bid - p.n_dp, p.sk_wgs);
+        u_next = rstart(w_me);
+        u_end = rstart(w_me + 1);
+    }
+    // ---- one piece per iteration: a whole item, or key tiles [t0, t1) of one
+    for (bool first_piece = true;; first_piece = false) {
+    int item, t0 = 0;
+    if (dp) {
+        if (!first_piece) break;
+        item = xcd_order(bid, p.n_dp);
+    } else {
+        if (u_next >= u_end) break;
+        locate(p.tail_unit0 + u_next, item, t0);
+    }
+    if (!first_piece) __syncthreads();      // the previous piece is done with LDS
     const int hq = item / p.total_tiles;
     const int tile = item - hq * p.total_tiles;
     int b = 0;
@@ -202,12 +279,6 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     const int q_slots = p.rows[b].q_slots;
     const int q_real = p.rows[b].q_real;
     const int m0 = (tile - p.rows[b].tile_start) * kBM;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int j = lane & 31;                 // query column inside a 32-block
-    const int h = lane >> 5;                 // lane half
 
     uint16_t* const out_h = p.out + (int64_t)hq * p.o_hs;
 
@@ -222,7 +293,8 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         if (p.lse)
             for (int r = tid; r < rows; r += kThreads)
                 p.lse[(int64_t)hq * p.lse_ld + q_start + m0 + r] = -INFINITY;
-        return;
+        u_next += 1;
+        continue;
     }
 
     const int hk = hq / p.group;
@@ -249,6 +321,12 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     const int npart = X == 0 ? 0 : (X <= kBN ? 1 : 2);
     const int n0 = npart == 0 ? kBN : (npart == 1 ? X : X - kBN);
     const int ntiles = npart + Pf + Rf;
+    // This piece: key tiles [t0, t1); it is the whole item unless cut.
+    const int t1 = dp ? ntiles : (int)min((int64_t)ntiles, (int64_t)t0 + (u_end - u_next));
+    u_next += t1 - t0;
+    const int nt = t1 - t0;
+    const bool whole = t0 == 0 && t1 == ntiles;
+    const bool mask_first = t0 == 0;           // only absolute tile 0 has masked rows
 
     // ---- Q fragments (B operand of S^T = K Q^T): lane (j, h) holds
     //      q[row j][16*ds + 8*h .. +7] for every k-step ds.  Rows past the
@@ -346,13 +424,19 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         r = uniform_rsrc(u32x4_t{(uint32_t)b, (uint32_t)(b >> 32), r[2], 0x00020000u});
     };
     // Job J of the copy of the current full tile: even J = K of op J/2, odd = V.
+    // LDS byte address of this wave's rows in buffer 0 (K and V); a tile
+    // slot and an op add a compile-time offset.
+    const uint32_t kdst0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(lds_k + wave * kOpsPerWave * kRowsPerOp * D));
+    const uint32_t vdst0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(lds_v + wave * kOpsPerWave * kRowsPerOp * D));
     auto fast_job = [&](auto SLOT, auto J) __attribute__((always_inline)) {
         constexpr int i = decltype(J)::value / 2;
-        const int row0 = (wave * kOpsPerWave + i) * kRowsPerOp;
+        constexpr int off = (decltype(SLOT)::value * kTile + i * kRowsPerOp * D) * 2;
         if constexpr (decltype(J)::value % 2 == 0)
-            lds_copy16_buf(rsk, koff[i], kbuf(SLOT) + row0 * D);
+            lds_copy16_buf<off>(rsk, koff[i], kdst0);
         else
-            lds_copy16_buf(rsv, voff[i], vbuf(SLOT) + row0 * D);
+            lds_copy16_buf<off>(rsv, voff[i], vdst0);
     };
     // Whole-tile copy issued at once (before the loop).
     auto dma_tile_now = [&](int t, auto SLOT) __attribute__((always_inline)) {
@@ -545,7 +629,9 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
                 vlo[step][0], vlo[step][1], vlo[step][2], vlo[step][3],
                 vhi[step][0], vhi[step][1], vhi[step][2], vhi[step][3]});
             o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, qb == 0 ? pc0[u] : p1[u], o[qb][db], 0, 0, 0);
-            if constexpr (i == 0 && decltype(MASK_NEXT)::value) mask_head(sn, decltype(KBN)::value);
+            if constexpr (i == 0 && decltype(MASK_NEXT)::value) {
+                if (mask_first) mask_head(sn, decltype(KBN)::value);
+            }
             static_for<16>([&](auto R) __attribute__((always_inline)) {
                 if constexpr (decltype(R)::value * kYSlots / 16 == i) w_step(sn[0], m_ref[0], w0, R);
             });
@@ -558,13 +644,13 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         pack_frags(w0.pk, pn0);
     };
 
-    // ---- prologue: tiles 0..2 into LDS; scores, reference max and the first
-    //      query block's weights of unit (0, 0).
+    // ---- prologue: the piece's tiles t0..t0+2 into LDS; scores, reference
+    //      max and the first query block's weights of its first unit.
     f32x16_t sA[kQB], sB[kQB];
     bf16x8_t pA0[2], pB0[2];
-    dma_tile_now(0, ic<0>{});
-    dma_tile_now(min(1, ntiles - 1), ic<1>{});
-    dma_tile_now(min(2, ntiles - 1), ic<2>{});
+    dma_tile_now(t0, ic<0>{});
+    dma_tile_now(t0 + min(1, nt - 1), ic<1>{});
+    dma_tile_now(t0 + min(2, nt - 1), ic<2>{});
     // tiles 0 and 1 must have landed; tile 2 may still be in flight
     tile_barrier();
 #pragma unroll
@@ -574,7 +660,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         for (int qb = 0; qb < kQB; ++qb)
             sA[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ds], ds == 0 ? f32x16_t{} : sA[qb], 0, 0, 0);
     }
-    mask_head(sA, 0);
+    if (mask_first) mask_head(sA, 0);
     m_ref[0] = unit_max(sA[0]);
     m_ref[1] = unit_max(sA[1]);
     {
@@ -586,18 +672,17 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds) kq[ds] = read_k(ic<0>{}, ic<1>{}, ds);
 
-    // ---- one 64-key tile in buffer S (of 4): units (t,0) and (t,1); tile t+3
-    //      is fetched into buffer S+3 meanwhile (clamped to the last tile, so
-    //      the copy is always of real keys).  On the last tile the look-ahead
-    //      of unit (t,1) reads a stale buffer; its reference update is
-    //      suppressed and its weights are never used.
-    auto body = [&](int t, auto S, auto FIRST) __attribute__((always_inline)) {
+    // ---- one 64-key tile (the piece's r-th) in buffer S (of 4): units (r,0)
+    //      and (r,1); tile r+3 is fetched into buffer S+3 meanwhile.  On the
+    //      last tile the look-ahead of unit (r,1) reads a stale buffer; its
+    //      reference update is suppressed and its weights are never used.
+    auto body = [&](int r, auto S, auto FIRST) __attribute__((always_inline)) {
         constexpr int s = decltype(S)::value;
         constexpr int s1 = (s + 1) % 4, s3 = (s + 3) % 4;
-        // Copy state for tile t+3 (always a full tile): advance 64 rows, or
-        // switch to the suffix, or an empty resource past the last tile.
-        const int tt = t + 3;
-        if (tt >= ntiles) {
+        // Copy state for tile r+3 (never tile 0, so a full tile): advance 64
+        // rows, or switch to the suffix, or an empty resource past the end.
+        const int tt = t0 + r + 3;
+        if (r + 3 >= nt) {
             rsk[2] = 0u;
             rsv[2] = 0u;
         } else if (tt == npart + Pf) {
@@ -611,61 +696,178 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         unit(ic<s>{}, ic<1>{}, ic<s>{}, ic<0>{}, ic<s1>{}, ic<0>{}, sA, sB, pA0, pB0, true, FIRST,
              copy_jobs);
         unit(ic<s1>{}, ic<0>{}, ic<s>{}, ic<1>{}, ic<s1>{}, ic<1>{}, sB, sA, pB0, pA0,
-             t + 1 < ntiles, std::false_type{}, no_jobs);
-        // Tiles up to t+2 must have landed before the barrier (tile t+2 is
-        // first read in the next tile); this tile's own prefetch (t+3, the
+             r + 1 < nt, std::false_type{}, no_jobs);
+        // Tiles up to r+2 must have landed before the barrier (tile r+2 is
+        // first read in the next tile); this tile's own prefetch (r+3, the
         // last kOpsPerWave*2 loads) may stay in flight.
         tile_barrier();
     };
     body(0, ic<0>{}, std::true_type{});
-    int t = 1;
-    for (; t + 4 <= ntiles; t += 4) {
-        body(t, ic<1>{}, std::false_type{});
-        body(t + 1, ic<2>{}, std::false_type{});
-        body(t + 2, ic<3>{}, std::false_type{});
-        body(t + 3, ic<0>{}, std::false_type{});
+    int r = 1;
+    for (; r + 4 <= nt; r += 4) {
+        body(r, ic<1>{}, std::false_type{});
+        body(r + 1, ic<2>{}, std::false_type{});
+        body(r + 2, ic<3>{}, std::false_type{});
+        body(r + 3, ic<0>{}, std::false_type{});
     }
-    if (t < ntiles) body(t++, ic<1>{}, std::false_type{});
-    if (t < ntiles) body(t++, ic<2>{}, std::false_type{});
-    if (t < ntiles) body(t++, ic<3>{}, std::false_type{});
+    if (r < nt) body(r++, ic<1>{}, std::false_type{});
+    if (r < nt) body(r++, ic<2>{}, std::false_type{});
+    if (r < nt) body(r++, ic<3>{}, std::false_type{});
     // No tile copy may still be landing in LDS when the wave ends.
     __builtin_amdgcn_s_waitcnt(0);
 
-    // ---- epilogue: normalise, bf16 round-to-nearest-even, pad rows as zeros.
-    //      O^T accumulator register r of lane half h is feature
-    //      32*db + 8*(r/4) + 4*h + r%4.
+    // ---- epilogue of a whole item: normalise, bf16 round-to-nearest-even,
+    //      pad rows as zeros.  O^T accumulator register r of lane half h is
+    //      feature 32*db + 8*(r/4) + 4*h + r%4.
+    if (whole) {
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        const int qi = m0 + wave * (kQB * 32) + qb * 32 + j;
-        if (qi >= q_slots) continue;
-        const bool real = qi < q_real;
-        const float l_tot = other_half_sum(l_sum[qb]);
-        const float inv = 1.0f / l_tot;
-        uint16_t* dst = out_h + (int64_t)(q_start + qi) * p.o_ts + 4 * h;
+        for (int qb = 0; qb < kQB; ++qb) {
+            const int qi = m0 + wave * (kQB * 32) + qb * 32 + j;
+            if (qi >= q_slots) continue;
+            const bool real = qi < q_real;
+            const float l_tot = other_half_sum(l_sum[qb]);
+            const float inv = 1.0f / l_tot;
+            uint16_t* dst = out_h + (int64_t)(q_start + qi) * p.o_ts + 4 * h;
 #pragma unroll
-        for (int db = 0; db < kDB; ++db)
+            for (int db = 0; db < kDB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2_t w = {pack_bf16(o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv),
-                             pack_bf16(o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv)};
-                if (!real) w = u32x2_t{0u, 0u};             // pad row: +0.0
-                *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = w;
-            }
-        if (p.lse && h == 0)
-            p.lse[(int64_t)hq * p.lse_ld + q_start + qi] =
-                real ? (m_ref[qb] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+                for (int g = 0; g < 4; ++g) {
+                    u32x2_t w = {pack_bf16(o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv),
+                                 pack_bf16(o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv)};
+                    if (!real) w = u32x2_t{0u, 0u};             // pad row: +0.0
+                    *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = w;
+                }
+            if (p.lse && h == 0)
+                p.lse[(int64_t)hq * p.lse_ld + q_start + qi] =
+                    real ? (m_ref[qb] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+        }
+        continue;
     }
+
+    // ---- a piece of a cut item: its O / l (fp32) and LSE (log2 units) go to
+    //      the piece's workspace slot (slot 2w when it is the first piece of
+    //      range w, else 2w + 1); jpa_merge_kernel combines them afterwards.
+    {
+        const int64_t A = item_unit(item) - p.tail_unit0;       // first tail unit of the item
+        const int slot = A <= rstart(w_me) ? 2 * w_me : 2 * w_me + 1;
+        float* const so = p.ws_o + (size_t)slot * kBM * D;
+        float* const sl = p.ws_lse + (size_t)slot * kBM;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            const int row = wave * (kQB * 32) + qb * 32 + j;
+            const float l_tot = other_half_sum(l_sum[qb]);
+            const float inv = 1.0f / l_tot;
+#pragma unroll
+            for (int db = 0; db < kDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<float4*>(so + (size_t)row * D + 32 * db + 8 * g + 4 * h) =
+                        make_float4(o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv,
+                                    o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv);
+            if (h == 0) sl[row] = m_ref[qb] + __builtin_amdgcn_logf(l_tot);
+        }
+    }
+    }   // pieces
+}
+
+// Merge of the cut items: one workgroup per item of the split part of the
+// launch (items n_dp ..), one thread per query row.  The pieces of an item are
+// those of ranges w_first .. w_last (a piece is slot 2w when it is the first
+// piece of range w, else 2w + 1); they are combined in range order with the
+// log-sum-exp merge of softmax partials:
+//   lse = log2 sum_k 2^lse_k,  out = sum_k 2^(lse_k - lse) * O_k.
+// Items that no range cut were written by jpa_fwd_kernel and are skipped.
+template <int D>
+__global__ __launch_bounds__(kBM, 1)
+void jpa_merge_kernel(const jpa_kernel_params p) {
+    constexpr int kCH = D / 8;
+    const int item = p.n_dp + blockIdx.x;
+    const int hq = item / p.total_tiles;
+    const int tile = item - hq * p.total_tiles;
+    int b = 0;
+    while (b + 1 < p.nrows && p.rows[b + 1].tile_start <= tile) ++b;
+    const int m0 = (tile - p.rows[b].tile_start) * kBM;
+    if (m0 >= p.rows[b].q_real) return;              // all-pad item: written directly
+    // first tail unit of the item (units: jpa_kernel_params)
+    int64_t A = (int64_t)hq * p.head_units;
+    for (int rb = 0; rb < p.nrows; ++rb) {
+        const int nt = (p.rows[rb].q_slots + kBM - 1) / kBM;
+        const int nr = (p.rows[rb].q_real + kBM - 1) / kBM;
+        const int nk = (p.rows[rb].keys + kBN - 1) / kBN;
+        const int tr = tile - p.rows[rb].tile_start;
+        if (tr < nt) {
+            A += tr < nr ? (int64_t)tr * nk : (int64_t)nr * nk + (tr - nr);
+            break;
+        }
+        A += (int64_t)nr * nk + (nt - nr);
+    }
+    A -= p.tail_unit0;
+    const int64_t ntiles = (p.rows[b].keys + kBN - 1) / kBN;
+    const int64_t skn = p.sk_wgs;
+    const int w_first = (int)(((A + 1) * skn - 1) / p.tail_units);
+    const int w_last = (int)(((A + ntiles) * skn - 1) / p.tail_units);
+    if (w_first == w_last) return;                   // whole item: written directly
+    auto slot_of = [&](int w) { return A <= w * p.tail_units / skn ? 2 * w : 2 * w + 1; };
+
+    const int qi = m0 + (int)threadIdx.x;
+    if (qi >= p.rows[b].q_slots) return;
+    uint16_t* dst = p.out + (int64_t)hq * p.o_hs + (int64_t)(p.rows[b].q_start + qi) * p.o_ts;
+    float* lse = p.lse ? p.lse + (int64_t)hq * p.lse_ld + p.rows[b].q_start + qi : nullptr;
+    if (qi >= p.rows[b].q_real) {                    // pad row
+        for (int c = 0; c < kCH; ++c) *reinterpret_cast<u32x4_t*>(dst + 8 * c) = u32x4_t{0u, 0u, 0u, 0u};
+        if (lse) *lse = -INFINITY;
+        return;
+    }
+    float mx = -INFINITY;
+    for (int w = w_first; w <= w_last; ++w)
+        mx = fmaxf(mx, p.ws_lse[(size_t)slot_of(w) * kBM + threadIdx.x]);
+    float sum = 0.f;
+    for (int w = w_first; w <= w_last; ++w)
+        sum += __builtin_amdgcn_exp2f(p.ws_lse[(size_t)slot_of(w) * kBM + threadIdx.x] - mx);
+    const float lse2 = mx + __builtin_amdgcn_logf(sum);
+    for (int c = 0; c < kCH; ++c) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int w = w_first; w <= w_last; ++w) {
+            const int sw = slot_of(w);
+            const float a = __builtin_amdgcn_exp2f(p.ws_lse[(size_t)sw * kBM + threadIdx.x] - lse2);
+            const float* src = p.ws_o + ((size_t)sw * kBM + threadIdx.x) * D + 8 * c;
+            const float4 x0 = *reinterpret_cast<const float4*>(src);
+            const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+            acc[0] += a * x0.x; acc[1] += a * x0.y; acc[2] += a * x0.z; acc[3] += a * x0.w;
+            acc[4] += a * x1.x; acc[5] += a * x1.y; acc[6] += a * x1.z; acc[7] += a * x1.w;
+        }
+        *reinterpret_cast<u32x4_t*>(dst + 8 * c) =
+            u32x4_t{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
+                    pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7])};
+    }
+    if (lse) *lse = lse2 * 0.69314718055994531f;
 }
 
 }  // namespace
 
 int jpa_launch_kernel(const jpa_kernel_params& p, int head_dim, void* stream) {
-    const int blocks = p.total_tiles * p.hq;
+    const int blocks = p.n_dp + p.sk_wgs;
     if (blocks == 0) return (int)hipSuccess;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (head_dim == 128)
         hipLaunchKernelGGL(jpa_fwd_kernel<128>, dim3(blocks), dim3(kThreads), 0, s, p);
     else
         hipLaunchKernelGGL(jpa_fwd_kernel<64>, dim3(blocks), dim3(kThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.sk_wgs == 0) return (int)e;
+    // the items of the split part that ranges cut are merged by a second
+    // kernel on the same stream (it sees the partials once the first ends)
+    const int tail_items = p.total_tiles * p.hq - p.n_dp;
+    if (head_dim == 128)
+        hipLaunchKernelGGL(jpa_merge_kernel<128>, dim3(tail_items), dim3(kBM), 0, s, p);
+    else
+        hipLaunchKernelGGL(jpa_merge_kernel<64>, dim3(tail_items), dim3(kBM), 0, s, p);
     return (int)hipGetLastError();
+}
+
+int jpa_device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return cus;
 }

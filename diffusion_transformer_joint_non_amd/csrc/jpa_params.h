@@ -3,6 +3,7 @@
 #ifndef JPA_PARAMS_H
 #define JPA_PARAMS_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 // Batch rows carried by one launch (their plan travels in the kernel
@@ -38,10 +39,32 @@ struct jpa_kernel_params {
     int32_t nrows;              // rows in this launch
     int32_t total_tiles;        // query tiles over those rows (per head)
     float c;                    // scale * log2(e)
+    // Work split.  The first n_dp workgroups each take one whole item (query
+    // head, query tile) in an XCD-grouped order.  The next sk_wgs workgroups
+    // split the remaining items (n_dp .. hq*total_tiles-1) into balanced
+    // contiguous ranges of "units": a real item counts its key tiles, an
+    // all-pad item counts 1.  The pieces of an item cut between ranges leave
+    // partial results in the workspace, merged by a second kernel.
+    int32_t n_dp;               // whole-item workgroups
+    int32_t sk_wgs;             // balanced-range workgroups (0: none)
+    int64_t head_units;         // units of one query head (all rows of the launch)
+    int64_t tail_unit0;         // absolute unit of item n_dp (hq*head_units + ..)
+    int64_t tail_units;         // units of items n_dp ..
+    float* ws_o;                // [2*sk_wgs][JPA_BLOCK_M][head_dim] partial outputs
+    float* ws_lse;              // [2*sk_wgs][JPA_BLOCK_M] partial LSE (log2 units)
     jpa_kernel_row rows[JPA_MAX_ROWS];
 };
 
+// Workspace layout for up to `wgs` balanced-range workgroups (bytes; every
+// part 256-byte aligned).
+inline size_t jpa_ws_o_bytes(int wgs, int head_dim) {
+    return (size_t)2 * wgs * JPA_BLOCK_M * head_dim * sizeof(float);
+}
+inline size_t jpa_ws_lse_bytes(int wgs) { return (size_t)2 * wgs * JPA_BLOCK_M * sizeof(float); }
+
 // Enqueue one launch; returns the hipError_t of the launch as an int.
 int jpa_launch_kernel(const jpa_kernel_params& p, int head_dim, void* stream);
+// Compute units of the current device, or 0 if the runtime reports none.
+int jpa_device_cus();
 
 #endif

@@ -27,7 +27,8 @@ JPA_ERR_HIP = 7
 JPA_DTYPE_BF16 = 1
 BLOCK_M = 256          # query rows per workgroup (for launch accounting only)
 
-EXPORTED = ("jpa_forward", "jpa_validate", "jpa_plan", "jpa_status_str", "jpa_abi_version")
+EXPORTED = ("jpa_forward", "jpa_forward_ws", "jpa_workspace_bytes", "jpa_validate", "jpa_plan",
+            "jpa_status_str", "jpa_abi_version")
 
 
 class JpaTensor(ctypes.Structure):
@@ -84,6 +85,12 @@ def load_library() -> ctypes.CDLL:
     lib.jpa_forward.restype = ctypes.c_int
     lib.jpa_forward.argtypes = [tp, tp, tp, tp, tp, ctypes.c_int32, i32p, i32p, i32p,
                                 ctypes.c_float, tp, ctypes.c_void_p, ctypes.c_void_p]
+    lib.jpa_forward_ws.restype = ctypes.c_int
+    lib.jpa_forward_ws.argtypes = [tp, tp, tp, tp, tp, ctypes.c_int32, i32p, i32p, i32p,
+                                   ctypes.c_float, tp, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]
+    lib.jpa_workspace_bytes.restype = ctypes.c_size_t
+    lib.jpa_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
     lib.jpa_validate.restype = ctypes.c_int
     lib.jpa_validate.argtypes = [tp, tp, tp, tp, tp, ctypes.c_int32, i32p, i32p, i32p,
                                  ctypes.c_float, tp, ctypes.c_void_p]
@@ -175,6 +182,73 @@ def jpa_validate(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix, cu_
                             None if lse is None else ctypes.c_void_p(lse.data_ptr()))
 
 
+def jpa_workspace_bytes(head_dim: int, split_wgs: int = 0) -> int:
+    """Workspace bytes jpa_forward_ws needs (split_wgs 0: the current device's
+    compute units); 0 if head_dim is unsupported or the device unknown."""
+    return int(load_library().jpa_workspace_bytes(int(head_dim), int(split_wgs)))
+
+
+_workspaces = {}
+
+
+def workspace_for(device, stream_handle: int, head_dim: int = 128, split_wgs: int = 0):
+    """A zero-filled workspace for jpa_forward_ws, cached per (device, stream,
+    split_wgs): calls on one stream are ordered, so they may share it."""
+    import torch
+    dev = torch.device(device)
+    key = (dev.index, int(stream_handle), int(split_wgs), int(head_dim))
+    ws = _workspaces.get(key)
+    if ws is None:
+        n = jpa_workspace_bytes(head_dim, split_wgs)
+        if n == 0:
+            raise JpaError(JPA_ERR_HIP, "cannot size the workspace for this device")
+        ws = torch.zeros(n, dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def _prepare(q, out, lse, with_lse, stream):
+    import torch
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None and with_lse:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (q.shape[1], q.shape[0])):
+        raise JpaArgumentError(JPA_ERR_SHAPE, "lse must be contiguous fp32 [Hq, Tq]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return out, lse, handle
+
+
+def jpa_forward_ws(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix, cu_suffix_real,
+                   scale: float, out=None, lse=None, stream=None, with_lse: bool = True,
+                   workspace="auto", split_wgs: int = 0):
+    """jpa_forward with a workspace that balances the last round of work over
+    every compute unit.  ``workspace``: "auto" (a cached zero-filled buffer
+    per device and stream), a uint8 CUDA tensor of at least
+    jpa_workspace_bytes() bytes whose counters are zero, or None (then the
+    call is jpa_forward's).  Returns (out, lse)."""
+    lib = load_library()
+    cq, cp, cs, batch, d = _common(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix,
+                                   cu_suffix_real)
+    out, lse, handle = _prepare(q, out, lse, with_lse, stream)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", a tensor or None')
+        workspace = workspace_for(q.device, handle, q.shape[2], split_wgs)
+    ws_ptr = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    od = descriptor(out)
+    st = lib.jpa_forward_ws(*[ctypes.byref(x) for x in d], batch, _i32p(cq), _i32p(cp), _i32p(cs),
+                            float(scale), ctypes.byref(od),
+                            None if lse is None else ctypes.c_void_p(lse.data_ptr()),
+                            ws_ptr, ws_bytes, int(split_wgs), ctypes.c_void_p(handle))
+    _raise_for(st)
+    return out, lse
+
+
 def jpa_forward(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix, cu_suffix_real,
                 scale: float, out=None, lse=None, stream=None, with_lse: bool = True):
     """Enqueue the attention on ``stream`` (default: torch's current stream).
@@ -183,21 +257,11 @@ def jpa_forward(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix, cu_s
     (HIP) tensors or views with contiguous head_dim.  cu_* are host offsets
     (lists, numpy arrays or CPU tensors).  Returns (out, lse); out/lse are
     allocated here only when not given."""
-    import torch
     lib = load_library()
     cq, cp, cs, batch, d = _common(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix,
                                    cu_suffix_real)
-    if out is None:
-        out = torch.empty_like(q, memory_format=torch.contiguous_format)
-    if lse is None and with_lse:
-        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
-                            or tuple(lse.shape) != (q.shape[1], q.shape[0])):
-        raise JpaArgumentError(JPA_ERR_SHAPE, "lse must be contiguous fp32 [Hq, Tq]")
+    out, lse, handle = _prepare(q, out, lse, with_lse, stream)
     od = descriptor(out)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     st = lib.jpa_forward(*[ctypes.byref(x) for x in d], batch, _i32p(cq), _i32p(cp), _i32p(cs),
                          float(scale), ctypes.byref(od),
                          None if lse is None else ctypes.c_void_p(lse.data_ptr()),

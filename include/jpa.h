@@ -37,6 +37,7 @@
 #ifndef JPA_H
 #define JPA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -148,6 +149,52 @@ JPA_API jpa_status jpa_forward(const jpa_tensor* q,
                                float scale,
                                const jpa_tensor* out, float* lse,
                                void* stream);
+
+/*
+ * jpa_forward_ws -- jpa_forward with a workspace that lets the last, partial
+ * round of work items be balanced over every compute unit.
+ *
+ * Work items are (query head, 256-query tile).  When their number is not a
+ * multiple of the compute-unit count, the last round would leave units idle;
+ * with a workspace, the key tiles of that round's items are cut into
+ * split_wgs equal ranges, one per workgroup, and every item cut between
+ * ranges is merged from per-piece
+ * partial results by a second kernel (the standard log-sum-exp merge of
+ * softmax partials, in a fixed order, so results do not depend on timing).
+ * The attention computed is the same as jpa_forward's; values may differ from
+ * it by rounding only.
+ *
+ *   workspace        device memory of at least jpa_workspace_bytes(head_dim,
+ *                    split_wgs) bytes, 256-byte aligned, or NULL (then this is
+ *                    jpa_forward).  No contents are needed between calls; the
+ *                    pieces' partial results pass through it to a second
+ *                    kernel enqueued on the same stream, so calls that may run
+ *                    at the same time need distinct workspaces.
+ *   workspace_bytes  its size; a smaller size than required is JPA_ERR_VALUE.
+ *   split_wgs        0: ranges = compute units, and the last round is cut
+ *                    only when it would leave more than half of them idle
+ *                    (each cut piece pays a prologue and a merge); > 0: that
+ *                    many ranges, always cut (a tuning and testing knob).
+ * Errors as jpa_forward, plus JPA_ERR_LAYOUT for a misaligned workspace and
+ * JPA_ERR_HIP when the device cannot be queried.
+ */
+JPA_API jpa_status jpa_forward_ws(const jpa_tensor* q,
+                                  const jpa_tensor* k_prefix, const jpa_tensor* v_prefix,
+                                  const jpa_tensor* k_suffix, const jpa_tensor* v_suffix,
+                                  int32_t batch,
+                                  const int32_t* cu_q, const int32_t* cu_prefix,
+                                  const int32_t* cu_suffix_real,
+                                  float scale,
+                                  const jpa_tensor* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, int32_t split_wgs,
+                                  void* stream);
+
+/*
+ * jpa_workspace_bytes -- workspace size jpa_forward_ws needs for head_dim
+ * (64 or 128) and split_wgs (0: the current device's compute units); 0 for an
+ * unsupported head_dim or when the device cannot be queried.
+ */
+JPA_API size_t jpa_workspace_bytes(int32_t head_dim, int32_t split_wgs);
 
 /*
  * jpa_validate -- every check jpa_forward performs, on the host only; never

@@ -218,6 +218,37 @@ def test_kv_token_stride_limit():
     assert check(0, 1 << 23) == jpa.JPA_OK       # queries are not limited
 
 
+def test_workspace_size_and_errors():
+    lib = jpa.load_library()
+    # partial outputs [2*wgs][256][D] fp32 + partial LSE [2*wgs][256] fp32
+    for d in (64, 128):
+        for wgs in (1, 8, 256):
+            assert jpa.jpa_workspace_bytes(d, wgs) == 2 * wgs * 256 * d * 4 + 2 * wgs * 256 * 4
+    assert jpa.jpa_workspace_bytes(96, 8) == 0
+    kw = _valid_call()
+    d = [jpa.descriptor(kw[n]) for n in ("q", "k_prefix", "v_prefix", "k_suffix", "v_suffix")]
+    od = jpa.descriptor(kw["out"])
+    cq, cp, cs = (np.asarray(kw[n], np.int32) for n in ("cu_q", "cu_prefix", "cu_suffix_real"))
+    P = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    need = jpa.jpa_workspace_bytes(64, 8)
+    buf = np.zeros(need + 512, np.uint8)
+    base = buf.ctypes.data
+    aligned = (base + 255) // 256 * 256
+
+    def call(ptr, nbytes, wgs):
+        return lib.jpa_forward_ws(*[ctypes.byref(x) for x in d], 2, P(cq), P(cp), P(cs), 0.1,
+                                  ctypes.byref(od), None, ctypes.c_void_p(ptr), nbytes, wgs, None)
+
+    assert call(aligned + 16, need, 8) == jpa.JPA_ERR_LAYOUT        # not 256-byte aligned
+    assert call(aligned, need - 1, 8) == jpa.JPA_ERR_VALUE          # too small
+    assert call(aligned, need, -1) == jpa.JPA_ERR_VALUE             # negative split
+    # argument errors come first, before any workspace or device question
+    bad = np.asarray([1, 5, 9], np.int32)
+    assert lib.jpa_forward_ws(*[ctypes.byref(x) for x in d], 2, P(bad), P(cp), P(cs), 0.1,
+                              ctypes.byref(od), None, ctypes.c_void_p(aligned + 16), need, 8,
+                              None) == jpa.JPA_ERR_SEGMENTS
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a GPU")
 def test_forward_without_gpu_reports_hip_error():
     kw = _valid_call()
