@@ -134,8 +134,10 @@ template <int OFF>
 __device__ __forceinline__ void lds_copy16_buf(u32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
     rsrc = u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
                    (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
-    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(rsrc), "s"(lds_base), "n"(OFF) : "memory", "m0", "scc");
+    uint32_t m0_out;       // m0 is written here: an output, so nothing else is kept in it
+    asm volatile("s_add_u32 m0, %3, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 : "={m0}"(m0_out) : "v"(voff), "s"(rsrc), "s"(lds_base), "n"(OFF) : "memory", "scc");
+    (void)m0_out;
 }
 
 // A wave-uniform 64-bit value in scalar registers.
