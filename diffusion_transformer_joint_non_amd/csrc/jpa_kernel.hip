@@ -46,6 +46,13 @@
 // * Work items are mapped so that the workgroups resident on one XCD (blocks
 //   are dealt round-robin over the 8 XCDs) cover consecutive query tiles of
 //   the same head, which then stream the same K/V through that XCD's L2.
+// * Optional balanced last round: when the item count leaves the last round
+//   of workgroups mostly idle, the items of that round are laid end to end
+//   as a run of key tiles and cut into one equal range per workgroup.  A
+//   range that covers an item whole writes it directly; pieces of an item
+//   write fp32 O, row sum and log2 LSE to a workspace, and a second small
+//   kernel on the same stream merges each split item's (at most a few)
+//   pieces in key order.  No cross-workgroup synchronisation inside a launch.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
