@@ -158,6 +158,53 @@ __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
 }
 
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// One wave's 64 output rows as bf16.  Register r of o[qb][db] in lane
+// (j, h) is row 32*qb + j, feature 32*db + 8*(r/4) + 4*h + r%4; it is scaled
+// by scale[qb] and rounded to nearest even.  The fragments go through the
+// wave's own LDS region (64 x D bf16, 16-byte chunks XOR-swizzled by row) so
+// that every global store writes whole rows, 16 contiguous bytes a lane,
+// instead of 8-byte pieces of 32 rows.  Rows at or past n_real are written
+// as +0.0, rows at or past n_slots are not written.
+template <int D>
+__device__ __forceinline__ void store_rows_bf16(const f32x16_t (&o)[kQB][D / 32], const float (&scale)[kQB],
+                                                lds_u16* lds, uint16_t* out_row0, int64_t o_ts,
+                                                int n_real, int n_slots, int lane) {
+    constexpr int kCH = D / 8;               // 16-byte chunks per row
+    constexpr int kDB = D / 32;
+    constexpr int kRowsPerRead = 64 / kCH;
+    const int j = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+        const int row = 32 * qb + j;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = 4 * db + g;
+                const u32x2_t w = {pack_bf16(o[qb][db][4 * g] * scale[qb], o[qb][db][4 * g + 1] * scale[qb]),
+                                   pack_bf16(o[qb][db][4 * g + 2] * scale[qb], o[qb][db][4 * g + 3] * scale[qb])};
+                *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
+                    lds + row * D + ((c ^ (row & (kCH - 1))) * 8) + 4 * h) = w;
+            }
+    }
+    // the reads below see this wave's own writes (LDS operations of a wave
+    // complete in order); the clobber keeps the compiler from moving them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < kCH; ++i) {
+        const int row = i * kRowsPerRead + lane / kCH;
+        const int c = lane % kCH;
+        u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+            lds + row * D + ((c ^ (row & (kCH - 1))) * 8));
+        if (row < n_slots) {
+            if (row >= n_real) v = u32x4_t{0u, 0u, 0u, 0u};        // pad row: +0.0
+            *reinterpret_cast<u32x4_t*>(out_row0 + (int64_t)row * o_ts + 8 * c) = v;
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1)
 void jpa_fwd_kernel(const jpa_kernel_params p) {
@@ -726,29 +773,28 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     __builtin_amdgcn_s_waitcnt(0);
 
     // ---- epilogue of a whole item: normalise, bf16 round-to-nearest-even,
-    //      pad rows as zeros.  O^T accumulator register r of lane half h is
-    //      feature 32*db + 8*(r/4) + 4*h + r%4.
+    //      pad rows as zeros, rows written whole through LDS (every wave is
+    //      done with the K/V tiles after the barrier; wave w uses K buffer w).
     if (whole) {
+        __syncthreads();
+        const int r0 = m0 + wave * (kQB * 32);
+        float l_tot[kQB], inv[kQB];
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
-            const int qi = m0 + wave * (kQB * 32) + qb * 32 + j;
-            if (qi >= q_slots) continue;
-            const bool real = qi < q_real;
-            const float l_tot = other_half_sum(l_sum[qb]);
-            const float inv = 1.0f / l_tot;
-            uint16_t* dst = out_h + (int64_t)(q_start + qi) * p.o_ts + 4 * h;
+            l_tot[qb] = other_half_sum(l_sum[qb]);
+            inv[qb] = 1.0f / l_tot[qb];
+        }
+        store_rows_bf16<D>(o, inv, (lds_u16*)(lds_k + wave * kTile), out_h + (int64_t)(q_start + r0) * p.o_ts,
+                           p.o_ts, q_real - r0, q_slots - r0, lane);
+        if (p.lse && h == 0) {
 #pragma unroll
-            for (int db = 0; db < kDB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    u32x2_t w = {pack_bf16(o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv),
-                                 pack_bf16(o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv)};
-                    if (!real) w = u32x2_t{0u, 0u};             // pad row: +0.0
-                    *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = w;
-                }
-            if (p.lse && h == 0)
-                p.lse[(int64_t)hq * p.lse_ld + q_start + qi] =
-                    real ? (m_ref[qb] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+            for (int qb = 0; qb < kQB; ++qb) {
+                const int qi = r0 + qb * 32 + j;
+                if (qi < q_slots)
+                    p.lse[(int64_t)hq * p.lse_ld + q_start + qi] =
+                        qi < q_real ? (m_ref[qb] + __builtin_amdgcn_logf(l_tot[qb])) * 0.69314718055994531f
+                                    : -INFINITY;
+            }
         }
         continue;
     }
@@ -756,40 +802,42 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     // ---- a piece of a cut item: its O / l (fp32) and LSE (log2 units) go to
     //      the piece's workspace slot (slot 2w when it is the first piece of
     //      range w, else 2w + 1); jpa_merge_kernel combines them afterwards.
+    //      O is kept in fragment order, float4 (qb, db, g) of lane l at
+    //      ((qb * kDB + db) * 4 + g) * 64 + l of the wave's part: each store
+    //      writes 1 KB contiguous.
     {
         const int64_t A = item_unit(item) - p.tail_unit0;       // first tail unit of the item
         const int slot = A <= rstart(w_me) ? 2 * w_me : 2 * w_me + 1;
-        float* const so = p.ws_o + (size_t)slot * kBM * D;
-        float* const sl = p.ws_lse + (size_t)slot * kBM;
+        float* const so = p.ws_o + (size_t)slot * kBM * D + (size_t)wave * (kQB * 32) * D;
+        float* const sl = p.ws_lse + (size_t)slot * kBM + wave * (kQB * 32);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
-            const int row = wave * (kQB * 32) + qb * 32 + j;
             const float l_tot = other_half_sum(l_sum[qb]);
             const float inv = 1.0f / l_tot;
 #pragma unroll
             for (int db = 0; db < kDB; ++db)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    *reinterpret_cast<float4*>(so + (size_t)row * D + 32 * db + 8 * g + 4 * h) =
+                    *reinterpret_cast<float4*>(so + ((size_t)((qb * kDB + db) * 4 + g) * 64 + lane) * 4) =
                         make_float4(o[qb][db][4 * g] * inv, o[qb][db][4 * g + 1] * inv,
                                     o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv);
-            if (h == 0) sl[row] = m_ref[qb] + __builtin_amdgcn_logf(l_tot);
+            if (h == 0) sl[qb * 32 + j] = m_ref[qb] + __builtin_amdgcn_logf(l_tot);
         }
     }
     }   // pieces
 }
 
 // Merge of the cut items: one workgroup per item of the split part of the
-// launch (items n_dp ..), one thread per query row.  The pieces of an item are
-// those of ranges w_first .. w_last (a piece is slot 2w when it is the first
-// piece of range w, else 2w + 1); they are combined in range order with the
-// log-sum-exp merge of softmax partials:
+// launch (items n_dp ..), its waves and lanes holding the same rows and
+// features as in jpa_fwd_kernel.  The pieces of an item are those of ranges
+// w_first .. w_last (a piece is slot 2w when it is the first piece of range
+// w, else 2w + 1); they are combined in range order with the log-sum-exp
+// merge of softmax partials:
 //   lse = log2 sum_k 2^lse_k,  out = sum_k 2^(lse_k - lse) * O_k.
 // Items that no range cut were written by jpa_fwd_kernel and are skipped.
 template <int D>
 __global__ __launch_bounds__(kBM, 1)
 void jpa_merge_kernel(const jpa_kernel_params p) {
-    constexpr int kCH = D / 8;
     const int item = p.n_dp + blockIdx.x;
     const int hq = item / p.total_tiles;
     const int tile = item - hq * p.total_tiles;
@@ -818,38 +866,64 @@ void jpa_merge_kernel(const jpa_kernel_params p) {
     if (w_first == w_last) return;                   // whole item: written directly
     auto slot_of = [&](int w) { return A <= w * p.tail_units / skn ? 2 * w : 2 * w + 1; };
 
-    const int qi = m0 + (int)threadIdx.x;
-    if (qi >= p.rows[b].q_slots) return;
-    uint16_t* dst = p.out + (int64_t)hq * p.o_hs + (int64_t)(p.rows[b].q_start + qi) * p.o_ts;
-    float* lse = p.lse ? p.lse + (int64_t)hq * p.lse_ld + p.rows[b].q_start + qi : nullptr;
-    if (qi >= p.rows[b].q_real) {                    // pad row
-        for (int c = 0; c < kCH; ++c) *reinterpret_cast<u32x4_t*>(dst + 8 * c) = u32x4_t{0u, 0u, 0u, 0u};
-        if (lse) *lse = -INFINITY;
-        return;
+    constexpr int kDB = D / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t lds_o[kWaves * 64 * D];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 31;
+    const int r0 = m0 + wave * (kQB * 32);                 // first row of this wave
+    float lse2[kQB];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+        const int row = wave * (kQB * 32) + qb * 32 + j;
+        float mx = -INFINITY;
+        for (int w = w_first; w <= w_last; ++w) mx = fmaxf(mx, p.ws_lse[(size_t)slot_of(w) * kBM + row]);
+        float sum = 0.f;
+        for (int w = w_first; w <= w_last; ++w)
+            sum += __builtin_amdgcn_exp2f(p.ws_lse[(size_t)slot_of(w) * kBM + row] - mx);
+        lse2[qb] = mx + __builtin_amdgcn_logf(sum);
     }
-    float mx = -INFINITY;
-    for (int w = w_first; w <= w_last; ++w)
-        mx = fmaxf(mx, p.ws_lse[(size_t)slot_of(w) * kBM + threadIdx.x]);
-    float sum = 0.f;
-    for (int w = w_first; w <= w_last; ++w)
-        sum += __builtin_amdgcn_exp2f(p.ws_lse[(size_t)slot_of(w) * kBM + threadIdx.x] - mx);
-    const float lse2 = mx + __builtin_amdgcn_logf(sum);
-    for (int c = 0; c < kCH; ++c) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int w = w_first; w <= w_last; ++w) {
-            const int sw = slot_of(w);
-            const float a = __builtin_amdgcn_exp2f(p.ws_lse[(size_t)sw * kBM + threadIdx.x] - lse2);
-            const float* src = p.ws_o + ((size_t)sw * kBM + threadIdx.x) * D + 8 * c;
-            const float4 x0 = *reinterpret_cast<const float4*>(src);
-            const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-            acc[0] += a * x0.x; acc[1] += a * x0.y; acc[2] += a * x0.z; acc[3] += a * x0.w;
-            acc[4] += a * x1.x; acc[5] += a * x1.y; acc[6] += a * x1.z; acc[7] += a * x1.w;
+    f32x16_t o[kQB][kDB];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) o[qb][db] = f32x16_t{};
+    for (int w = w_first; w <= w_last; ++w) {
+        const int sw = slot_of(w);
+        const float* const so = p.ws_o + (size_t)sw * kBM * D + (size_t)wave * (kQB * 32) * D;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            const float a = __builtin_amdgcn_exp2f(
+                p.ws_lse[(size_t)sw * kBM + wave * (kQB * 32) + qb * 32 + j] - lse2[qb]);
+#pragma unroll
+            for (int db = 0; db < kDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 x =
+                        *reinterpret_cast<const float4*>(so + ((size_t)((qb * kDB + db) * 4 + g) * 64 + lane) * 4);
+                    o[qb][db][4 * g] += a * x.x;
+                    o[qb][db][4 * g + 1] += a * x.y;
+                    o[qb][db][4 * g + 2] += a * x.z;
+                    o[qb][db][4 * g + 3] += a * x.w;
+                }
         }
-        *reinterpret_cast<u32x4_t*>(dst + 8 * c) =
-            u32x4_t{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
-                    pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7])};
     }
-    if (lse) *lse = lse2 * 0.69314718055994531f;
+    float one[kQB];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) one[qb] = 1.f;
+    const int q_start = p.rows[b].q_start, q_real = p.rows[b].q_real, q_slots = p.rows[b].q_slots;
+    store_rows_bf16<D>(o, one, (lds_u16*)(lds_o + wave * 64 * D),
+                       p.out + (int64_t)hq * p.o_hs + (int64_t)(q_start + r0) * p.o_ts, p.o_ts,
+                       q_real - r0, q_slots - r0, lane);
+    if (p.lse && lane < 32) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            const int qi = r0 + qb * 32 + j;
+            if (qi < q_slots)
+                p.lse[(int64_t)hq * p.lse_ld + q_start + qi] =
+                    qi < q_real ? lse2[qb] * 0.69314718055994531f : -INFINITY;
+        }
+    }
 }
 
 }  // namespace
