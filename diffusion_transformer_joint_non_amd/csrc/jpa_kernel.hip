@@ -396,12 +396,6 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
 #pragma unroll
         for (int ds = 0; ds < kDS; ++ds) qf[qb][ds] = __builtin_bit_cast(bf16x8_t, load16(src + 16 * ds));
     }
-    // Register classes: Q fragments and the O accumulators live in AGPRs (only
-    // MFMAs touch them in the loop); the softmax VALU work uses VGPRs.
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-        for (int ds = 0; ds < kDS; ++ds) asm("" : "+a"(qf[qb][ds]));
 
     // ---- global -> LDS tile loads, 16 bytes per lane straight into LDS
     //      (lane l of a wave lands at base + 16*l).  A wave instruction (an
@@ -707,6 +701,14 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     dma_tile_now(t0, ic<0>{});
     dma_tile_now(t0 + min(1, nt - 1), ic<1>{});
     dma_tile_now(t0 + min(2, nt - 1), ic<2>{});
+    // Register classes: Q fragments and the O accumulators live in AGPRs (only
+    // MFMAs touch them in the loop); the softmax VALU work uses VGPRs.  Pinned
+    // only here, after the tile copies are issued: the pin waits for the Q
+    // loads, and the copies then travel alongside them.
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int ds = 0; ds < kDS; ++ds) asm("" : "+a"(qf[qb][ds]));
     // tiles 0 and 1 must have landed; tile 2 may still be in flight
     tile_barrier();
 #pragma unroll
