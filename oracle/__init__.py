@@ -18,3 +18,9 @@ from .fp64 import (  # noqa: F401
     valid_flops,
     widen,
 )
+from .qk_norm_rope import (  # noqa: F401
+    apply_rope,
+    qk_norm_rope,
+    rms_norm,
+    rope_pairs,
+)

@@ -17,3 +17,9 @@ from .workloads import (  # noqa: F401
     TENSOR_NAMES,
     custom_workload,
 )
+from .norm_rope import (  # noqa: F401
+    NORM_ROPE_WORKLOADS,
+    NormRopeWorkload,
+    make_norm_rope_inputs,
+    rope_table,
+)
