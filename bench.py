@@ -3,6 +3,7 @@
 attention forward (libjpa, gfx950) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload 2]
+    python bench.py --op norm_rope [--workload 4]
 
 One step = one jpa_forward_ws call over the whole workload (all query rows of
 all heads, inputs already resident in HBM).  Prints ONE JSON line:
@@ -16,6 +17,10 @@ all heads, inputs already resident in HBM).  Prints ONE JSON line:
 
 Options for profiling runs: --no-cpu-baseline, --copy-probe BYTES (time a plain
 device copy of that many bytes; used to calibrate rocprofv3 HBM counters).
+
+--op norm_rope measures the step before attention instead: per-head Q/K
+RMSNorm + rotary embedding (jpa_qk_norm_rope) on the q/k shapes of a norm-rope
+workload; value is GB/s of algorithmic HBM bytes, roofline against 8 TB/s.
 """
 
 import argparse
@@ -38,28 +43,35 @@ KERNEL_SOURCES = ("diffusion_transformer_joint_non_amd/csrc/jpa_kernel.hip",
                   "diffusion_transformer_joint_non_amd/csrc/jpa_params.h")
 DEFAULT_WORKLOAD = 2
 
+NR_METRIC = "Q/K RMSNorm+RoPE GB/s (algorithmic HBM bytes) + % of MI355X HBM peak"
+PEAK_HBM_GBS = 8000.0            # MI355X published HBM3E bandwidth
+NR_KERNEL_NAME = "jpa_norm_rope_kernel"
+NR_KERNEL_SOURCES = ("diffusion_transformer_joint_non_amd/csrc/jpa_norm_rope.hip",
+                     "diffusion_transformer_joint_non_amd/csrc/jpa_norm_rope_params.h")
+NR_DEFAULT_WORKLOAD = 4
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload_name: str):
+def load_traffic(workload_name: str, kernel=KERNEL_NAME, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when there is none or the kernel changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload_name}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_name}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -127,12 +139,98 @@ def copy_probe(nbytes: int, steps: int):
                       "ms": dt * 1e3, "GB/s": 2 * n * 2 / dt / 1e9}), flush=True)
 
 
+def bench_norm_rope(args):
+    """One step = one jpa_qk_norm_rope call over all q and k rows."""
+    import torch
+    import synth
+    from diffusion_transformer_joint_non_amd import jpa
+
+    wid = NR_DEFAULT_WORKLOAD if args.workload is None else args.workload
+    w = synth.NORM_ROPE_WORKLOADS[wid]
+    log(f"norm-rope workload {w.wid} {w.name}: generating inputs")
+    x = synth.make_norm_rope_inputs(w)
+    to_dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k = to_dev(x["q"]), to_dev(x["k"])
+    wq, wk = torch.from_numpy(x["q_weight"]).cuda(), torch.from_numpy(x["k_weight"]).cuda()
+    table = torch.from_numpy(x["table"]).cuda()
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    stream = torch.cuda.current_stream()
+    # algorithmic bytes: q and k read and written once, the table and weights read once
+    nbytes = (2 * 2 * w.tokens * (w.hq + w.hkv) * w.d + 4 * w.tokens * w.rotary_dim + 2 * 4 * w.d)
+
+    def step():
+        jpa.jpa_qk_norm_rope(q, k, wq, wk, table, w.rotary_dim, w.interleaved, w.eps,
+                             q_out=qo, k_out=ko, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = np.asarray([e0.elapsed_time(e1) for e0, e1 in ev])
+    ms_per_step = wall * 1e3 / args.steps
+    kern_ms = float(np.mean(per_launch_ms))
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    result = {
+        "metric": NR_METRIC,
+        "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"norm_rope_{w.name}", "tokens": w.tokens, "heads_q": w.hq,
+                   "heads_kv": w.hkv, "head_dim": w.d, "rotary_dim": w.rotary_dim,
+                   "pairs": "interleaved" if w.interleaved else "half-split",
+                   "algorithmic_bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": load_traffic(w.name, NR_KERNEL_NAME, NR_KERNEL_SOURCES),
+                     "kernel": NR_KERNEL_NAME,
+                     "kernel_ms": {"mean": round(kern_ms, 4),
+                                   "median": round(float(np.median(per_launch_ms)), 4),
+                                   "min": round(float(per_launch_ms.min()), 4),
+                                   "max": round(float(per_launch_ms.max()), 4)},
+                     "kernel_source_sha256_16": kernel_source_hash(NR_KERNEL_SOURCES)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline: timing the fp64 oracle on a token sample")
+        n_tok = min(w.tokens, 4096)
+        tokens = np.sort(np.random.default_rng(5151).choice(w.tokens, n_tok, replace=False))
+        f64 = lambda b: synth.bf16_bits_to_f32(b).astype(np.float64)
+        qs, ks, ts = f64(x["q"][tokens]), f64(x["k"][tokens]), x["table"][tokens].astype(np.float64)
+        t0 = time.perf_counter()
+        rq, rk = oracle.qk_norm_rope(qs, ks, x["q_weight"], x["k_weight"], ts, w.rotary_dim,
+                                     w.interleaved, w.eps)
+        dt = time.perf_counter() - t0
+        sub_bytes = nbytes * n_tok / w.tokens
+        result["cpu_baseline"] = {"value": round(sub_bytes / dt / 1e9, 3), "unit": "GB/s",
+                                  "cores": blas_threads(), "kind": "oracle",
+                                  "sample": f"seeded subset: {n_tok} of {w.tokens} tokens, every head",
+                                  "seconds": round(dt, 3)}
+        idx = torch.from_numpy(tokens).cuda()
+        gq = qo.index_select(0, idx).float().cpu().numpy()
+        gk = ko.index_select(0, idx).float().cpu().numpy()
+        rel = max(float(np.max(np.abs(gq - rq) / (np.abs(rq) + 1e-6))),
+                  float(np.max(np.abs(gk - rk) / (np.abs(rk) + 1e-6))))
+        result["parity"] = {"max_abs": float(f"{max(np.abs(gq - rq).max(), np.abs(gk - rk).max()):.3e}"),
+                            "max_rel_1e-6": float(f"{rel:.3e}")}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", type=int, default=None)
+    ap.add_argument("--op", choices=("attention", "norm_rope"), default="attention")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
@@ -150,10 +248,14 @@ def main():
         copy_probe(args.copy_probe, max(args.steps, 1))
         return
 
+    if args.op == "norm_rope":
+        bench_norm_rope(args)
+        return
+
     import synth
     from diffusion_transformer_joint_non_amd import jpa
 
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS[DEFAULT_WORKLOAD if args.workload is None else args.workload]
     log(f"workload {w.wid} {w.name}: generating inputs")
     x = synth.make_inputs(w)
     dev = {n: torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(torch.bfloat16).cuda()

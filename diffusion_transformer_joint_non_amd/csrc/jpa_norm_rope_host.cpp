@@ -1,0 +1,118 @@
+// Host front end of jpa_qk_norm_rope: argument checks (host only, before any
+// HIP call) and the launch.
+#include <cmath>
+#include <cstdint>
+
+#include "jpa.h"
+#include "jpa_norm_rope.h"
+#include "jpa_norm_rope_params.h"
+
+namespace {
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+jpa_status check_view(const jpa_tensor* t, int64_t tokens, int32_t heads, int32_t head_dim) {
+    if (!t) return JPA_ERR_NULL;
+    if (t->dtype != JPA_DTYPE_BF16) return JPA_ERR_DTYPE;
+    if (t->head_dim != head_dim || t->heads != heads || t->tokens != tokens || heads <= 0) return JPA_ERR_SHAPE;
+    if (!t->data && t->tokens > 0) return JPA_ERR_NULL;
+    if (!aligned(t->data, 16)) return JPA_ERR_LAYOUT;
+    if (t->token_stride % 8 != 0 || t->head_stride % 8 != 0) return JPA_ERR_LAYOUT;
+    if (t->head_stride < t->head_dim) return JPA_ERR_LAYOUT;
+    if (t->token_stride < (int64_t)t->heads * t->head_stride) return JPA_ERR_LAYOUT;
+    return JPA_OK;
+}
+
+// Element extent of a view: [data, data + span) in bf16 elements, and the
+// span of one token's row of heads.
+int64_t row_span(const jpa_tensor* t) { return (int64_t)(t->heads - 1) * t->head_stride + t->head_dim; }
+int64_t span(const jpa_tensor* t) {
+    return t->tokens == 0 ? 0 : (t->tokens - 1) * t->token_stride + row_span(t);
+}
+
+bool same_view(const jpa_tensor* a, const jpa_tensor* b) {
+    return a->data == b->data && a->tokens == b->tokens && a->heads == b->heads &&
+           a->token_stride == b->token_stride && a->head_stride == b->head_stride;
+}
+
+// True when no element of a is an element of b.  Views of one buffer with the
+// same token stride (e.g. the q and k slices of a fused QKV tensor) are
+// disjoint when their per-token column windows do not meet.
+bool disjoint(const jpa_tensor* a, const jpa_tensor* b) {
+    if (a->tokens == 0 || b->tokens == 0) return true;
+    const intptr_t pa = reinterpret_cast<intptr_t>(a->data), pb = reinterpret_cast<intptr_t>(b->data);
+    const intptr_t ea = pa + 2 * span(a), eb = pb + 2 * span(b);
+    if (ea <= pb || eb <= pa) return true;
+    if (a->token_stride != b->token_stride) return false;
+    const int64_t ts = a->token_stride;
+    int64_t d = (pb - pa) / 2;                 // element offset of b from a
+    if ((pb - pa) % 2 != 0) return false;
+    d %= ts;
+    if (d < 0) d += ts;                        // b's window starts d columns into a's token row
+    const int64_t wa = row_span(a), wb = row_span(b);
+    // windows [0, wa) and [d, d + wb) modulo ts must not intersect
+    return wa <= d && d + wb <= ts;
+}
+
+}  // namespace
+
+extern "C" {
+
+JPA_API jpa_status jpa_qk_norm_rope(const jpa_tensor* q, const jpa_tensor* k,
+                                    const float* q_weight, const float* k_weight,
+                                    const float* table, int64_t table_stride,
+                                    int32_t rotary_dim, int32_t interleaved, float eps,
+                                    const jpa_tensor* q_out, const jpa_tensor* k_out,
+                                    void* stream) {
+    if (!q || !k || !q_out || !k_out) return JPA_ERR_NULL;
+    const int32_t d = q->head_dim;
+    if (d != 64 && d != 128 && d != 256) return JPA_ERR_SHAPE;
+    jpa_status st;
+    if ((st = check_view(q, q->tokens, q->heads, d)) != JPA_OK) return st;
+    if ((st = check_view(k, q->tokens, k->heads, d)) != JPA_OK) return st;
+    if ((st = check_view(q_out, q->tokens, q->heads, d)) != JPA_OK) return st;
+    if ((st = check_view(k_out, q->tokens, k->heads, d)) != JPA_OK) return st;
+    if (!q_weight || !k_weight) return JPA_ERR_NULL;
+    if (!aligned(q_weight, 16) || !aligned(k_weight, 16)) return JPA_ERR_LAYOUT;
+    if (rotary_dim < 0 || rotary_dim > d || rotary_dim % 2 != 0) return JPA_ERR_SHAPE;
+    if (interleaved != 0 && interleaved != 1) return JPA_ERR_VALUE;
+    if (!std::isfinite(eps) || eps < 0.f) return JPA_ERR_VALUE;
+    if (rotary_dim > 0) {
+        if (!table && q->tokens > 0) return JPA_ERR_NULL;
+        if (!aligned(table, 4)) return JPA_ERR_LAYOUT;
+        if (table_stride < rotary_dim) return JPA_ERR_LAYOUT;
+    }
+    // outputs: each is its own input, or shares no element with any input;
+    // the two outputs share none either
+    if (!same_view(q_out, q) && !(disjoint(q_out, q) && disjoint(q_out, k))) return JPA_ERR_LAYOUT;
+    if (!same_view(k_out, k) && !(disjoint(k_out, k) && disjoint(k_out, q))) return JPA_ERR_LAYOUT;
+    if (same_view(q_out, q) && !disjoint(q_out, k)) return JPA_ERR_LAYOUT;
+    if (same_view(k_out, k) && !disjoint(k_out, q)) return JPA_ERR_LAYOUT;
+    if (!disjoint(q_out, k_out)) return JPA_ERR_LAYOUT;
+
+    jpa_norm_rope_params p{};
+    const jpa_tensor* in[2] = {q, k};
+    const jpa_tensor* out[2] = {q_out, k_out};
+    for (int s = 0; s < 2; ++s) {
+        p.x[s] = static_cast<const uint16_t*>(in[s]->data);
+        p.y[s] = static_cast<uint16_t*>(out[s]->data);
+        p.x_ts[s] = in[s]->token_stride;
+        p.y_ts[s] = out[s]->token_stride;
+        p.x_hs[s] = in[s]->head_stride;
+        p.y_hs[s] = out[s]->head_stride;
+        p.heads[s] = in[s]->heads;
+    }
+    p.w[0] = q_weight;
+    p.w[1] = k_weight;
+    p.table = table;
+    p.table_stride = table_stride;
+    p.rows_q = q->tokens * q->heads;
+    p.rows_total = p.rows_q + q->tokens * k->heads;
+    p.rotary_dim = rotary_dim;
+    p.interleaved = interleaved;
+    p.eps = eps;
+    if (p.rows_total == 0) return JPA_OK;
+    return jpa_launch_norm_rope(p, d, stream) == 0 ? JPA_OK : JPA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,4 +1,5 @@
-"""Thin ctypes binding over libjpa's C ABI (include/jpa.h), same names.
+"""Thin ctypes binding over libjpa's C ABI (include/jpa.h and
+include/jpa_norm_rope.h), same names.
 
 Argument marshalling only: every step of the attention runs in the HIP
 library.  PyTorch supplies device memory and the current stream; nothing else
@@ -28,7 +29,7 @@ JPA_DTYPE_BF16 = 1
 BLOCK_M = 256          # query rows per workgroup (for launch accounting only)
 
 EXPORTED = ("jpa_forward", "jpa_forward_ws", "jpa_workspace_bytes", "jpa_validate", "jpa_plan",
-            "jpa_status_str", "jpa_abi_version")
+            "jpa_status_str", "jpa_abi_version", "jpa_qk_norm_rope")
 
 
 class JpaTensor(ctypes.Structure):
@@ -101,6 +102,10 @@ def load_library() -> ctypes.CDLL:
     lib.jpa_status_str.argtypes = [ctypes.c_int]
     lib.jpa_abi_version.restype = ctypes.c_int32
     lib.jpa_abi_version.argtypes = []
+    vp = ctypes.c_void_p
+    lib.jpa_qk_norm_rope.restype = ctypes.c_int
+    lib.jpa_qk_norm_rope.argtypes = [tp, tp, vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_float, tp, tp, vp]
     _lib = lib
     return lib
 
@@ -268,3 +273,40 @@ def jpa_forward(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix, cu_s
                          ctypes.c_void_p(handle))
     _raise_for(st)
     return out, lse
+
+
+def jpa_qk_norm_rope(q, k, q_weight, k_weight, table, rotary_dim: int, interleaved: bool, eps: float,
+                     q_out=None, k_out=None, stream=None):
+    """Per-head RMSNorm of q [T, Hq, D] and k [T, Hkv, D] (bf16 CUDA tensors
+    or views) with float32 weights [D], then the rotary embedding from the
+    float32 table [T, >= rotary_dim] = [cos | sin] (interleaved or half-split
+    pairs).  q_out/k_out: outputs (allocated when None; pass q/k for in
+    place).  Returns (q_out, k_out)."""
+    import torch
+    lib = load_library()
+    for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
+        if w.dtype != torch.float32 or w.dim() != 1 or not w.is_contiguous():
+            raise JpaArgumentError(JPA_ERR_SHAPE, f"{name} must be a contiguous float32 [head_dim]")
+        if w.shape[0] != q.shape[2]:
+            raise JpaArgumentError(JPA_ERR_SHAPE, f"{name} must have head_dim entries")
+    table_ptr, table_stride = None, 0
+    if table is not None:
+        if table.dtype != torch.float32 or table.dim() != 2 or table.stride(1) != 1:
+            raise JpaArgumentError(JPA_ERR_SHAPE, "table must be float32 [T, >= rotary_dim], rows contiguous")
+        if table.shape[0] != q.shape[0] or table.shape[1] < rotary_dim:
+            raise JpaArgumentError(JPA_ERR_SHAPE, "table must be [T, >= rotary_dim]")
+        table_ptr, table_stride = ctypes.c_void_p(table.data_ptr()), table.stride(0)
+    if q_out is None:
+        q_out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if k_out is None:
+        k_out = torch.empty_like(k, memory_format=torch.contiguous_format)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    d = [descriptor(x) for x in (q, k, q_out, k_out)]
+    st = lib.jpa_qk_norm_rope(ctypes.byref(d[0]), ctypes.byref(d[1]), ctypes.c_void_p(q_weight.data_ptr()),
+                              ctypes.c_void_p(k_weight.data_ptr()), table_ptr, int(table_stride),
+                              int(rotary_dim), 1 if interleaved else 0, float(eps),
+                              ctypes.byref(d[2]), ctypes.byref(d[3]), ctypes.c_void_p(handle))
+    _raise_for(st)
+    return q_out, k_out

@@ -1,13 +1,16 @@
 """Host-side checks of the C ABI (no GPU needed; no kernel is run).
 
-* the in-tree libjpa.so loads and exports every function include/jpa.h declares;
+* the in-tree libjpa.so loads and exports every function include/*.h declares;
 * jpa_plan's integers equal the hand-derived workload bookkeeping and the
   oracle's decoding, bit for bit;
 * every validation error of jpa_validate is reachable from the host;
-* on a machine without a GPU, jpa_forward reports JPA_ERR_HIP instead of crashing.
+* on a machine without a GPU, jpa_forward reports JPA_ERR_HIP instead of crashing;
+* every argument check of jpa_qk_norm_rope is reachable from the host, and a
+  call that passes them reaches the launch (JPA_ERR_HIP without a GPU).
 """
 
 import ctypes
+import glob
 import json
 import os
 import re
@@ -25,8 +28,10 @@ HEADER = os.path.join(ROOT, "include", "jpa.h")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    return re.findall(r"JPA_API\s+[\w\s\*]+?\b(jpa_\w+)\s*\(", text)
+    names = []
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        names += re.findall(r"JPA_API\s+[\w\s\*]+?\b(jpa_\w+)\s*\(", open(h).read())
+    return names
 
 
 def test_library_exports_every_declared_symbol():
@@ -264,3 +269,100 @@ def test_forward_rejects_before_any_launch():
     with pytest.raises(jpa.JpaArgumentError) as e:
         jpa.jpa_forward(**kw, lse=torch.zeros(4, kw["q"].shape[0]), stream=0)
     assert e.value.status == jpa.JPA_ERR_VALUE
+
+
+# ---------------------------------------------------------------- jpa_qk_norm_rope
+
+_FAKE = 1 << 20            # 16-byte aligned host-side stand-in; never dereferenced
+
+
+def _nr_tensor(tokens, heads, d, base=_FAKE, ts=None, hs=None, dtype=jpa.JPA_DTYPE_BF16):
+    hs = d if hs is None else hs
+    ts = heads * hs if ts is None else ts
+    return jpa.JpaTensor(base, tokens, ts, heads, hs, d, dtype)
+
+
+def _nr_call(q, k, qo, ko, rot=96, il=0, eps=1e-6, wq=_FAKE, wk=_FAKE, table=_FAKE, tstride=96):
+    lib = jpa.load_library()
+    return lib.jpa_qk_norm_rope(ctypes.byref(q) if q else None, ctypes.byref(k) if k else None,
+                                ctypes.c_void_p(wq) if wq else None, ctypes.c_void_p(wk) if wk else None,
+                                ctypes.c_void_p(table) if table else None, tstride, rot, il, eps,
+                                ctypes.byref(qo) if qo else None, ctypes.byref(ko) if ko else None, None)
+
+
+def _nr_valid():
+    T, hq, hkv, d = 40, 4, 2, 128
+    q = _nr_tensor(T, hq, d, base=_FAKE)
+    k = _nr_tensor(T, hkv, d, base=_FAKE * 2)
+    qo = _nr_tensor(T, hq, d, base=_FAKE * 3)
+    ko = _nr_tensor(T, hkv, d, base=_FAKE * 4)
+    return q, k, qo, ko
+
+
+@pytest.mark.parametrize("case,code", [
+    ("null_q", jpa.JPA_ERR_NULL), ("null_kout", jpa.JPA_ERR_NULL), ("null_weight", jpa.JPA_ERR_NULL),
+    ("null_table", jpa.JPA_ERR_NULL), ("dtype", jpa.JPA_ERR_DTYPE), ("head_dim_96", jpa.JPA_ERR_SHAPE),
+    ("tokens_differ", jpa.JPA_ERR_SHAPE), ("out_heads", jpa.JPA_ERR_SHAPE), ("rot_odd", jpa.JPA_ERR_SHAPE),
+    ("rot_too_big", jpa.JPA_ERR_SHAPE), ("eps_negative", jpa.JPA_ERR_VALUE), ("eps_nan", jpa.JPA_ERR_VALUE),
+    ("interleaved_2", jpa.JPA_ERR_VALUE), ("weight_misaligned", jpa.JPA_ERR_LAYOUT),
+    ("table_stride", jpa.JPA_ERR_LAYOUT), ("data_misaligned", jpa.JPA_ERR_LAYOUT),
+    ("head_stride_small", jpa.JPA_ERR_LAYOUT), ("out_overlaps_in", jpa.JPA_ERR_LAYOUT),
+    ("qout_overlaps_k", jpa.JPA_ERR_LAYOUT), ("outs_overlap", jpa.JPA_ERR_LAYOUT),
+    ("fused_views_overlap", jpa.JPA_ERR_LAYOUT),
+])
+def test_norm_rope_rejects(case, code):
+    q, k, qo, ko = _nr_valid()
+    kw = {}
+    if case == "null_q": q = None
+    elif case == "null_kout": ko = None
+    elif case == "null_weight": kw["wk"] = 0
+    elif case == "null_table": kw["table"] = 0
+    elif case == "dtype": k.dtype = 0
+    elif case == "head_dim_96":
+        q, k, qo, ko = (_nr_tensor(40, h, 96, base=b) for h, b in ((4, _FAKE), (2, 2 * _FAKE), (4, 3 * _FAKE), (2, 4 * _FAKE)))
+    elif case == "tokens_differ": k.tokens = 39
+    elif case == "out_heads": qo.heads = 3
+    elif case == "rot_odd": kw["rot"] = 95
+    elif case == "rot_too_big": kw.update(rot=130, tstride=130)
+    elif case == "eps_negative": kw["eps"] = -1e-6
+    elif case == "eps_nan": kw["eps"] = float("nan")
+    elif case == "interleaved_2": kw["il"] = 2
+    elif case == "weight_misaligned": kw["wq"] = _FAKE + 4
+    elif case == "table_stride": kw["tstride"] = 80
+    elif case == "data_misaligned": q.data = _FAKE + 8
+    elif case == "head_stride_small": k.head_stride = 120
+    elif case == "out_overlaps_in": qo.data = _FAKE + 2 * 128
+    elif case == "qout_overlaps_k": qo.data = 2 * _FAKE
+    elif case == "outs_overlap": ko.data = 3 * _FAKE + 16
+    elif case == "fused_views_overlap":
+        # q and k slices of one fused buffer whose column windows meet
+        ts = (4 + 2 + 2) * 128
+        q = _nr_tensor(40, 4, 128, base=_FAKE, ts=ts)
+        k = _nr_tensor(40, 2, 128, base=_FAKE + 2 * 3 * 128, ts=ts)
+        qo, ko = q, k
+    assert _nr_call(q, k, qo, ko, **kw) == code
+
+
+def test_norm_rope_empty_is_a_no_op():
+    q, k, qo, ko = (_nr_tensor(0, h, 128, base=0) for h in (4, 2, 4, 2))
+    assert _nr_call(q, k, qo, ko, table=0) == jpa.JPA_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a GPU")
+@pytest.mark.parametrize("case", ["separate", "in_place", "fused_in_place", "no_rotary", "d64_interleaved"])
+def test_norm_rope_valid_calls_reach_the_launch(case):
+    q, k, qo, ko = _nr_valid()
+    kw = {}
+    if case == "in_place":
+        qo, ko = q, k
+    elif case == "fused_in_place":
+        ts = (4 + 2 + 2) * 128                 # [T, Hq + 2 Hkv, D] fused QKV, v untouched
+        q = _nr_tensor(40, 4, 128, base=_FAKE, ts=ts)
+        k = _nr_tensor(40, 2, 128, base=_FAKE + 2 * 4 * 128, ts=ts)
+        qo, ko = q, k
+    elif case == "no_rotary":
+        kw.update(rot=0, table=0, tstride=0)
+    elif case == "d64_interleaved":
+        q, k, qo, ko = (_nr_tensor(40, h, 64, base=b) for h, b in ((4, _FAKE), (2, 2 * _FAKE), (4, 3 * _FAKE), (2, 4 * _FAKE)))
+        kw.update(rot=48, il=1, tstride=48)
+    assert _nr_call(q, k, qo, ko, **kw) == jpa.JPA_ERR_HIP
