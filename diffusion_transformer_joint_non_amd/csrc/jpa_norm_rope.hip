@@ -12,8 +12,10 @@
 // * a row is head_dim/8 lanes, 16 contiguous bytes each (one dwordx4 load and
 //   one store per lane), so a wave covers 64*8/head_dim whole rows and every
 //   memory instruction is fully coalesced;
-// * the mean square is an in-lane sum of 8 squares plus a butterfly over the
-//   row's lanes; everything is fp32 and the result is rounded to bf16 once;
+// * the mean square is an in-lane sum of 8 squares plus a DPP reduction over
+//   the row's lanes; the reciprocal square root is the hardware one (about
+//   one fp32 ulp, far below the bf16 rounding); everything is fp32 and the
+//   result is rounded to bf16 once;
 // * interleaved pairs sit inside a lane; half-split partners are read back
 //   from the wave's own LDS copy of the normalised row;
 // * when rotary_dim and the table layout allow it (VEC), the table is read
@@ -21,7 +23,9 @@
 //   channel;
 // * one launch covers q and k: rows [0, rows_q) are q's, the rest k's, in
 //   token-major order so that a token's table row is read by neighbouring
-//   lanes; a grid-stride loop over groups of rows.
+//   lanes; a grid-stride loop over groups of rows, each lane issuing the
+//   loads of kUnroll rows (and their table entries) before using any, so
+//   enough bytes are in flight to cover HBM latency.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -31,19 +35,37 @@
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 4;                     // rows per lane with loads in flight together
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
-// fp32 -> bf16, round to nearest even (the inputs here are finite or NaN;
-// NaN stays NaN).
-__device__ __forceinline__ uint32_t to_bf16(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Sum over each aligned group of LANES lanes (8, 16 or 32), every lane of a
+// group getting the same value: DPP quad permutations, then the half-row and
+// row mirrors (the lanes being mirrored already hold equal partial sums, so
+// a mirror pairs the two halves), then one cross-row exchange for 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int LANES>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp_mov<0xB1>(v);                   // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);                   // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);                  // row_half_mirror
+    if constexpr (LANES >= 16) v += dpp_mov<0x140>(v);   // row_mirror
+    if constexpr (LANES >= 32) v += __shfl_xor(v, 16, 64);
+    return v;
 }
 
 template <int D, bool VEC>
@@ -59,7 +81,13 @@ __global__ __launch_bounds__(kThreads) void jpa_norm_rope_kernel(const jpa_norm_
     const int e0 = 8 * (lane % kLanes);        // first channel of this lane
     const int rot = p.rotary_dim;
     const int half = rot >> 1;
+    const bool il = p.interleaved != 0;
     float* const srow = stage[wave] + sub * D;
+    // VEC: this lane's 8 channels are all rotated or all passed through, and
+    // (half-split) all in the first or all in the second half
+    const bool rotated = e0 < rot;
+    const bool first_half = e0 < half;
+    const int i0 = il ? (e0 >> 1) : (first_half ? e0 : e0 - half);      // first pair index
 
     float wt[2][8];
 #pragma unroll
@@ -70,116 +98,144 @@ __global__ __launch_bounds__(kThreads) void jpa_norm_rope_kernel(const jpa_norm_
             wt[s][j] = v.x; wt[s][j + 1] = v.y; wt[s][j + 2] = v.z; wt[s][j + 3] = v.w;
         }
 
-    for (int64_t base = (int64_t)blockIdx.x * kRowsPerBlock; base < p.rows_total;
-         base += (int64_t)gridDim.x * kRowsPerBlock) {
-        const int64_t r = base + wave * kRowsPerWave + sub;
-        const bool active = r < p.rows_total;
-        const int s = r >= p.rows_q ? 1 : 0;
-        const int64_t rr = s ? r - p.rows_q : r;
-        const int heads = p.heads[s];
-        const int64_t t = active ? rr / heads : 0;
-        const int h = active ? (int)(rr - t * heads) : 0;
-
-        float y[8];
-        if (active) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p.x[s] + t * p.x_ts[s] + (int64_t)h * p.x_hs[s] + e0);
+    const int64_t step = (int64_t)gridDim.x * kRowsPerBlock * kUnroll;
+    for (int64_t base = (int64_t)blockIdx.x * kRowsPerBlock * kUnroll; base < p.rows_total; base += step) {
+        // issue every load of the group first: kUnroll rows per lane in flight
+        bool act[kUnroll];
+        int sel[kUnroll], hh[kUnroll];
+        int64_t tt[kUnroll];
+        u32x4_t xv[kUnroll];
+        float4 tc[kUnroll][2], ts[kUnroll][2];       // VEC table values (cos, sin)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) { y[2 * j] = bf16_lo(v[j]); y[2 * j + 1] = bf16_hi(v[j]); }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) y[j] = 0.f;
-        }
-        float ss = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss = fmaf(y[j], y[j], ss);
-#pragma unroll
-        for (int m = kLanes / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-        const float inv = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) y[j] = y[j] * inv * (s ? wt[1][j] : wt[0][j]);
-
-        if (rot > 0) {
-            const float* const tab = p.table + t * p.table_stride;
-            float part[8], cs[8], sn[8];
-            if (p.interleaved) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) part[j] = y[j ^ 1];
-            } else {
-                // the row's normalised channels through this wave's LDS rows
-                *reinterpret_cast<float4*>(srow + e0) = make_float4(y[0], y[1], y[2], y[3]);
-                *reinterpret_cast<float4*>(srow + e0 + 4) = make_float4(y[4], y[5], y[6], y[7]);
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                if constexpr (VEC) {
-                    if (e0 < rot) {
-                        const int pe = e0 < half ? e0 + half : e0 - half;
-                        const float4 a = *reinterpret_cast<const float4*>(srow + pe);
-                        const float4 b = *reinterpret_cast<const float4*>(srow + pe + 4);
-                        part[0] = a.x; part[1] = a.y; part[2] = a.z; part[3] = a.w;
-                        part[4] = b.x; part[5] = b.y; part[6] = b.z; part[7] = b.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int e = e0 + j;
-                        part[j] = e < half ? srow[e + half] : (e < rot ? srow[e - half] : 0.f);
-                    }
-                }
-                // the reads are done before the next group overwrites the rows
-                __builtin_amdgcn_wave_barrier();
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t r = base + u * kRowsPerBlock + wave * kRowsPerWave + sub;
+            act[u] = r < p.rows_total;
+            sel[u] = r >= p.rows_q ? 1 : 0;
+            // row of its tensor (< 2^31) -> (token, head) by multiply-shift
+            const uint32_t rr = act[u] ? (uint32_t)(sel[u] ? r - p.rows_q : r) : 0u;
+            // per-lane choice between the two tensors' scalar arguments (never
+            // an indexed read of the argument block, which would be a memory load)
+            const bool k_row = sel[u] != 0;
+            const uint32_t magic = k_row ? p.div_magic[1] : p.div_magic[0];
+            const int shift = k_row ? p.div_shift[1] : p.div_shift[0];
+            const uint32_t t32 = (uint32_t)(((uint64_t)rr * magic) >> shift);
+            tt[u] = t32;
+            hh[u] = (int)(rr - t32 * (uint32_t)(k_row ? p.heads[1] : p.heads[0]));
+            xv[u] = u32x4_t{0u, 0u, 0u, 0u};
+            if (act[u]) {
+                const uint16_t* const xb = k_row ? p.x[1] : p.x[0];
+                const uint32_t xts = (uint32_t)(k_row ? p.x_ts[1] : p.x_ts[0]);
+                const uint32_t xhs = (uint32_t)(k_row ? p.x_hs[1] : p.x_hs[0]);
+                xv[u] = *reinterpret_cast<const u32x4_t*>(xb + (uint64_t)t32 * xts + ((uint32_t)hh[u] * xhs + (uint32_t)e0));
             }
             if constexpr (VEC) {
-                if (e0 < rot && active) {
-                    const int i0 = p.interleaved ? (e0 >> 1) : (e0 < half ? e0 : e0 - half);
-                    if (p.interleaved) {
-                        const float4 c4 = *reinterpret_cast<const float4*>(tab + i0);
-                        const float4 s4 = *reinterpret_cast<const float4*>(tab + half + i0);
-                        const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, ssn[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) { cs[j] = cc[j >> 1]; sn[j] = ssn[j >> 1]; }
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 8; j += 4) {
-                            const float4 c4 = *reinterpret_cast<const float4*>(tab + i0 + j);
-                            const float4 s4 = *reinterpret_cast<const float4*>(tab + half + i0 + j);
-                            cs[j] = c4.x; cs[j + 1] = c4.y; cs[j + 2] = c4.z; cs[j + 3] = c4.w;
-                            sn[j] = s4.x; sn[j + 1] = s4.y; sn[j + 2] = s4.z; sn[j + 3] = s4.w;
-                        }
-                    }
-                    const bool first = p.interleaved ? true : e0 < half;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const bool a = p.interleaved ? (j & 1) == 0 : first;
-                        y[j] = a ? y[j] * cs[j] - part[j] * sn[j] : y[j] * cs[j] + part[j] * sn[j];
+                if (act[u] && rotated) {
+                    const float* const tab = p.table + (uint64_t)(uint32_t)tt[u] * (uint64_t)p.table_stride;
+                    tc[u][0] = *reinterpret_cast<const float4*>(tab + i0);
+                    ts[u][0] = *reinterpret_cast<const float4*>(tab + half + i0);
+                    if (!il) {
+                        tc[u][1] = *reinterpret_cast<const float4*>(tab + i0 + 4);
+                        ts[u][1] = *reinterpret_cast<const float4*>(tab + half + i0 + 4);
                     }
                 }
-            } else {
-                if (active) {
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int s = sel[u];
+            float y[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { y[2 * j] = bf16_lo(xv[u][j]); y[2 * j + 1] = bf16_hi(xv[u][j]); }
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ss = fmaf(y[j], y[j], ss);
+            ss = group_sum<kLanes>(ss);
+            const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] = y[j] * inv * (s ? wt[1][j] : wt[0][j]);
+
+            if (rot > 0) {
+                float part[8];
+                if (il) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) part[j] = y[j ^ 1];
+                } else {
+                    // the row's normalised channels through this wave's LDS rows
+                    *reinterpret_cast<float4*>(srow + e0) = make_float4(y[0], y[1], y[2], y[3]);
+                    *reinterpret_cast<float4*>(srow + e0 + 4) = make_float4(y[4], y[5], y[6], y[7]);
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    if constexpr (VEC) {
+                        const int pe = first_half ? e0 + half : e0 - half;
+                        if (rotated) {
+                            const float4 a4 = *reinterpret_cast<const float4*>(srow + pe);
+                            const float4 b4 = *reinterpret_cast<const float4*>(srow + pe + 4);
+                            part[0] = a4.x; part[1] = a4.y; part[2] = a4.z; part[3] = a4.w;
+                            part[4] = b4.x; part[5] = b4.y; part[6] = b4.z; part[7] = b4.w;
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const int e = e0 + j;
+                            part[j] = e < half ? srow[e + half] : (e < rot ? srow[e - half] : 0.f);
+                        }
+                    }
+                    // the reads are done before the next row overwrites the stage
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                }
+                if constexpr (VEC) {
+                    if (rotated && act[u]) {
+                        float cs[8], sn[8];
+                        if (il) {
+                            const float cc[4] = {tc[u][0].x, tc[u][0].y, tc[u][0].z, tc[u][0].w};
+                            const float sv[4] = {ts[u][0].x, ts[u][0].y, ts[u][0].z, ts[u][0].w};
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) { cs[j] = cc[j >> 1]; sn[j] = sv[j >> 1]; }
+                        } else {
+                            const float cc[8] = {tc[u][0].x, tc[u][0].y, tc[u][0].z, tc[u][0].w,
+                                                 tc[u][1].x, tc[u][1].y, tc[u][1].z, tc[u][1].w};
+                            const float sv[8] = {ts[u][0].x, ts[u][0].y, ts[u][0].z, ts[u][0].w,
+                                                 ts[u][1].x, ts[u][1].y, ts[u][1].z, ts[u][1].w};
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) { cs[j] = cc[j]; sn[j] = sv[j]; }
+                        }
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const bool a = il ? (j & 1) == 0 : first_half;
+                            y[j] = a ? y[j] * cs[j] - part[j] * sn[j] : y[j] * cs[j] + part[j] * sn[j];
+                        }
+                    }
+                } else if (act[u]) {
+                    const float* const tab = p.table + (uint64_t)(uint32_t)tt[u] * (uint64_t)p.table_stride;
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const int e = e0 + j;
                         if (e < rot) {
-                            const bool a = p.interleaved ? (e & 1) == 0 : e < half;
-                            const int i = p.interleaved ? (e >> 1) : (a ? e : e - half);
+                            const bool a = il ? (e & 1) == 0 : e < half;
+                            const int i = il ? (e >> 1) : (a ? e : e - half);
                             const float c = tab[i], sv = tab[half + i];
                             y[j] = a ? y[j] * c - part[j] * sv : y[j] * c + part[j] * sv;
                         }
                     }
                 }
             }
-        }
-        if (active) {
-            const u32x4_t o = {to_bf16(y[0]) | (to_bf16(y[1]) << 16), to_bf16(y[2]) | (to_bf16(y[3]) << 16),
-                               to_bf16(y[4]) | (to_bf16(y[5]) << 16), to_bf16(y[6]) | (to_bf16(y[7]) << 16)};
-            *reinterpret_cast<u32x4_t*>(p.y[s] + t * p.y_ts[s] + (int64_t)h * p.y_hs[s] + e0) = o;
+            if (act[u]) {
+                const u32x4_t o = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
+                                   pack_bf16(y[6], y[7])};
+                uint16_t* const yb = s ? p.y[1] : p.y[0];
+                const uint32_t yts = (uint32_t)(s ? p.y_ts[1] : p.y_ts[0]);
+                const uint32_t yhs = (uint32_t)(s ? p.y_hs[1] : p.y_hs[0]);
+                *reinterpret_cast<u32x4_t*>(yb + (uint64_t)(uint32_t)tt[u] * yts + ((uint32_t)hh[u] * yhs + (uint32_t)e0)) = o;
+            }
         }
     }
 }
 
 template <int D>
 int launch_d(const jpa_norm_rope_params& p, bool vec, hipStream_t s) {
-    constexpr int kRowsPerBlock = (64 / (D / 8)) * kWaves;
+    constexpr int kRowsPerBlock = (64 / (D / 8)) * kWaves * kUnroll;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

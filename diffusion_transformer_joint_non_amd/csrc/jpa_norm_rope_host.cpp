@@ -54,6 +54,18 @@ bool disjoint(const jpa_tensor* a, const jpa_tensor* b) {
     return wa <= d && d + wb <= ts;
 }
 
+// Division by an invariant d (1 <= d <= 2^16) for dividends below 2^31:
+// with l = ceil(log2 d) and m = ceil(2^(31+l) / d) < 2^32, floor(n / d) =
+// (n * m) >> (31 + l) for every such n (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, theorem 4.2).
+void div_magic(int32_t d, uint32_t* magic, int32_t* shift) {
+    int l = 0;
+    while ((int64_t(1) << l) < d) ++l;
+    const uint64_t num = uint64_t(1) << (31 + l);
+    *magic = (uint32_t)((num + (uint64_t)d - 1) / (uint64_t)d);
+    *shift = 31 + l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -89,6 +101,13 @@ JPA_API jpa_status jpa_qk_norm_rope(const jpa_tensor* q, const jpa_tensor* k,
     if (same_view(q_out, q) && !disjoint(q_out, k)) return JPA_ERR_LAYOUT;
     if (same_view(k_out, k) && !disjoint(k_out, q)) return JPA_ERR_LAYOUT;
     if (!disjoint(q_out, k_out)) return JPA_ERR_LAYOUT;
+    // rows of one tensor and token strides fit the kernel's 32-bit index math
+    if (q->heads > 65536 || k->heads > 65536) return JPA_ERR_SHAPE;
+    if (q->tokens * q->heads >= (int64_t(1) << 31) || q->tokens * k->heads >= (int64_t(1) << 31))
+        return JPA_ERR_SHAPE;
+    const jpa_tensor* all[4] = {q, k, q_out, k_out};
+    for (const jpa_tensor* t : all)
+        if (t->token_stride >= (int64_t(1) << 32)) return JPA_ERR_LAYOUT;
 
     jpa_norm_rope_params p{};
     const jpa_tensor* in[2] = {q, k};
@@ -101,6 +120,7 @@ JPA_API jpa_status jpa_qk_norm_rope(const jpa_tensor* q, const jpa_tensor* k,
         p.x_hs[s] = in[s]->head_stride;
         p.y_hs[s] = out[s]->head_stride;
         p.heads[s] = in[s]->heads;
+        div_magic(in[s]->heads, &p.div_magic[s], &p.div_shift[s]);
     }
     p.w[0] = q_weight;
     p.w[1] = k_weight;

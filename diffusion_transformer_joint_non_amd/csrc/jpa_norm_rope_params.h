@@ -13,6 +13,8 @@ struct jpa_norm_rope_params {
     int64_t x_ts[2], y_ts[2];    // token strides (elements)
     int32_t x_hs[2], y_hs[2];    // head strides (elements)
     int32_t heads[2];
+    uint32_t div_magic[2];       // row -> token: t = (row * div_magic) >> div_shift, exact
+    int32_t div_shift[2];        // for every row < 2^31 (rows of one tensor < 2^31)
     const float* w[2];           // per-channel norm weights, float [head_dim]
     const float* table;          // float [tokens, table_stride]: [cos | sin]
     int64_t table_stride;

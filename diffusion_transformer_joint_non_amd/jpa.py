@@ -290,7 +290,7 @@ def jpa_qk_norm_rope(q, k, q_weight, k_weight, table, rotary_dim: int, interleav
         if w.shape[0] != q.shape[2]:
             raise JpaArgumentError(JPA_ERR_SHAPE, f"{name} must have head_dim entries")
     table_ptr, table_stride = None, 0
-    if table is not None:
+    if table is not None and rotary_dim > 0:
         if table.dtype != torch.float32 or table.dim() != 2 or table.stride(1) != 1:
             raise JpaArgumentError(JPA_ERR_SHAPE, "table must be float32 [T, >= rotary_dim], rows contiguous")
         if table.shape[0] != q.shape[0] or table.shape[1] < rotary_dim:
