@@ -24,3 +24,9 @@ from .qk_norm_rope import (  # noqa: F401
     rms_norm,
     rope_pairs,
 )
+from .shard_plan import (  # noqa: F401
+    Shard,
+    build_shard_plan,
+    tail_attn_meta,
+    tail_segments,
+)
