@@ -4,6 +4,7 @@ attention forward (libjpa, gfx950) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload 2]
     python bench.py --op norm_rope [--workload 4]
+    python bench.py --op rank_share [--workload 4] [--sp 8] [--rank 0]
 
 One step = one jpa_forward_ws call over the whole workload (all query rows of
 all heads, inputs already resident in HBM).  Prints ONE JSON line:
@@ -21,6 +22,9 @@ device copy of that many bytes; used to calibrate rocprofv3 HBM counters).
 --op norm_rope measures the step before attention instead: per-head Q/K
 RMSNorm + rotary embedding (jpa_qk_norm_rope) on the q/k shapes of a norm-rope
 workload; value is GB/s of algorithmic HBM bytes, roofline against 8 TB/s.
+--op rank_share measures one rank's share of a head-parallel split of the
+attention workload over --sp ranks (Hq/sp and Hkv/sp heads over the whole
+sequence), the replicated prefix read through head-sliced views.
 """
 
 import argparse
@@ -225,7 +229,9 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=None)
-    ap.add_argument("--op", choices=("attention", "norm_rope"), default="attention")
+    ap.add_argument("--op", choices=("attention", "norm_rope", "rank_share"), default="attention")
+    ap.add_argument("--sp", type=int, default=8, help="rank_share: ranks of the head split")
+    ap.add_argument("--rank", type=int, default=0, help="rank_share: which rank's share")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
@@ -251,10 +257,31 @@ def main():
     from diffusion_transformer_joint_non_amd import jpa
 
     w = synth.WORKLOADS[DEFAULT_WORKLOAD if args.workload is None else args.workload]
+    share = None
+    if args.op == "rank_share":
+        # One rank's share of a head-parallel (Ulysses) split over args.sp ranks:
+        # Hq/sp query and Hkv/sp kv heads over the full sequence, with the
+        # prefix replicated on every rank in full and read through a
+        # head-sliced view (a pointer offset and the full token stride).
+        if w.hq % args.sp or w.hkv % args.sp:
+            print(f"--sp {args.sp} does not divide the heads {w.hq}/{w.hkv}", file=sys.stderr)
+            sys.exit(2)
+        full_hkv = w.hkv
+        w = synth.custom_workload(w.hq // args.sp, w.hkv // args.sp, w.d, w.prefix, w.suffix_real,
+                                  w.suffix_pad, w.queries, wid=w.wid, name=f"{w.name}_sp{args.sp}_rank")
+        share = {"sp": args.sp, "rank": args.rank, "heads_q_total": w.hq * args.sp,
+                 "heads_kv_total": full_hkv, "prefix_view": "head slice of the replicated prefix"}
     log(f"workload {w.wid} {w.name}: generating inputs")
     x = synth.make_inputs(w)
     dev = {n: torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(torch.bfloat16).cuda()
            for n in ("q", "k_prefix", "v_prefix", "k_suffix", "v_suffix")}
+    if share is not None:
+        h0 = args.rank * w.hkv
+        for n in ("k_prefix", "v_prefix"):
+            full = torch.zeros((dev[n].shape[0], share["heads_kv_total"], w.d), dtype=torch.bfloat16,
+                               device="cuda")
+            full[:, h0:h0 + w.hkv] = dev[n]
+            dev[n] = full[:, h0:h0 + w.hkv]          # a view: token stride of all heads
     rows, flops = jpa.jpa_plan(x["cu_q"], x["cu_prefix"], x["cu_suffix_real"], w.hq, w.d)
     out = torch.empty_like(dev["q"])
     lse = torch.empty((w.hq, dev["q"].shape[0]), dtype=torch.float32, device="cuda")
@@ -309,7 +336,7 @@ def main():
                    "head_dim": w.d, "prefix": list(map(int, w.prefix)),
                    "suffix_real": list(map(int, w.suffix_real)),
                    "suffix_pad": list(map(int, w.suffix_pad)), "queries": w.queries,
-                   "valid_flops": flops},
+                   "valid_flops": flops, **({"rank_share": share} if share else {})},
         "pct_of_bf16_peak": round(100.0 * flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -19,7 +19,8 @@ LIB_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIB_DIR, "libjpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["jpa_kernel.hip", "jpa_host.cpp", "jpa_norm_rope.hip", "jpa_norm_rope_host.cpp"]
+SOURCES = ["jpa_kernel.hip", "jpa_host.cpp", "jpa_norm_rope.hip", "jpa_norm_rope_host.cpp",
+           "jpa_shard_host.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -1,5 +1,5 @@
-"""Thin ctypes binding over libjpa's C ABI (include/jpa.h and
-include/jpa_norm_rope.h), same names.
+"""Thin ctypes binding over libjpa's C ABI (include/jpa.h,
+include/jpa_norm_rope.h and include/jpa_shard.h), same names.
 
 Argument marshalling only: every step of the attention runs in the HIP
 library.  PyTorch supplies device memory and the current stream; nothing else
@@ -29,7 +29,8 @@ JPA_DTYPE_BF16 = 1
 BLOCK_M = 256          # query rows per workgroup (for launch accounting only)
 
 EXPORTED = ("jpa_forward", "jpa_forward_ws", "jpa_workspace_bytes", "jpa_validate", "jpa_plan",
-            "jpa_status_str", "jpa_abi_version", "jpa_qk_norm_rope")
+            "jpa_status_str", "jpa_abi_version", "jpa_qk_norm_rope", "jpa_shard_plan",
+            "jpa_tail_attn_meta", "jpa_tail_segments")
 
 
 class JpaTensor(ctypes.Structure):
@@ -42,6 +43,12 @@ class JpaTensor(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
     ]
+
+
+class JpaShard(ctypes.Structure):
+    _fields_ = [("orig_len", ctypes.c_int64), ("local_len", ctypes.c_int64), ("num_pad", ctypes.c_int64),
+                ("sp_size", ctypes.c_int32), ("sp_rank", ctypes.c_int32), ("local_pad", ctypes.c_int64),
+                ("local_real_len", ctypes.c_int64)]
 
 
 class JpaRowPlan(ctypes.Structure):
@@ -102,6 +109,14 @@ def load_library() -> ctypes.CDLL:
     lib.jpa_status_str.argtypes = [ctypes.c_int]
     lib.jpa_abi_version.restype = ctypes.c_int32
     lib.jpa_abi_version.argtypes = []
+    sp = ctypes.POINTER(JpaShard)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.jpa_shard_plan.restype = ctypes.c_int
+    lib.jpa_shard_plan.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, sp]
+    lib.jpa_tail_attn_meta.restype = ctypes.c_int
+    lib.jpa_tail_attn_meta.argtypes = [sp, ctypes.c_int32, i32p, i64p, i64p]
+    lib.jpa_tail_segments.restype = ctypes.c_int
+    lib.jpa_tail_segments.argtypes = [sp, ctypes.c_int32, ctypes.c_int32, i32p, ctypes.c_int32, i32p, i32p, i32p]
     vp = ctypes.c_void_p
     lib.jpa_qk_norm_rope.restype = ctypes.c_int
     lib.jpa_qk_norm_rope.argtypes = [tp, tp, vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -310,3 +325,38 @@ def jpa_qk_norm_rope(q, k, q_weight, k_weight, table, rotary_dim: int, interleav
                               ctypes.byref(d[2]), ctypes.byref(d[3]), ctypes.c_void_p(handle))
     _raise_for(st)
     return q_out, k_out
+
+
+def jpa_shard_plan(seq_len: int, sp_size: int, sp_rank: int) -> JpaShard:
+    """Tail-padded even shard facts of rank sp_rank (host only)."""
+    lib = load_library()
+    out = JpaShard()
+    _raise_for(lib.jpa_shard_plan(int(seq_len), int(sp_size), int(sp_rank), ctypes.byref(out)))
+    return out
+
+
+def jpa_tail_attn_meta(shard: JpaShard, seqlen_multiplier: int = 1):
+    """None without pad, else {"tail", "valid_len", "max_seqlen_tail"}."""
+    lib = load_library()
+    has = ctypes.c_int32()
+    valid = ctypes.c_int64()
+    mx = ctypes.c_int64()
+    _raise_for(lib.jpa_tail_attn_meta(ctypes.byref(shard), int(seqlen_multiplier), ctypes.byref(has),
+                                      ctypes.byref(valid), ctypes.byref(mx)))
+    if not has.value:
+        return None
+    return {"tail": True, "valid_len": valid.value, "max_seqlen_tail": mx.value}
+
+
+def jpa_tail_segments(shard: JpaShard, seqlen_multiplier: int, prefix_lens, queries_include_prefix: bool):
+    """(cu_q, cu_prefix, cu_suffix_real) int32 arrays of one rank's attention call."""
+    lib = load_library()
+    pl = _i32(prefix_lens)
+    b = int(pl.size)
+    cu_q = np.zeros(b + 1, dtype=np.int32)
+    cu_p = np.zeros(b + 1, dtype=np.int32)
+    cu_s = np.zeros(2 * b + 1, dtype=np.int32)
+    _raise_for(lib.jpa_tail_segments(ctypes.byref(shard), int(seqlen_multiplier), b,
+                                     _i32p(pl) if b else None, 1 if queries_include_prefix else 0,
+                                     _i32p(cu_q), _i32p(cu_p), _i32p(cu_s)))
+    return cu_q, cu_p, cu_s
