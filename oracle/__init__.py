@@ -30,3 +30,4 @@ from .shard_plan import (  # noqa: F401
     tail_attn_meta,
     tail_segments,
 )
+from .cat_pad import cat_pad, out_shape  # noqa: F401

@@ -23,3 +23,4 @@ from .norm_rope import (  # noqa: F401
     make_norm_rope_inputs,
     rope_table,
 )
+from .cat_pad import CAT_PAD_CASES, CatPadCase, make_cat_pad_inputs  # noqa: F401
