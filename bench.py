@@ -5,6 +5,7 @@ attention forward (libjpa, gfx950) on one MI355X.
     python bench.py [--steps K] [--warmup W] [--workload 2]
     python bench.py --op norm_rope [--workload 4]
     python bench.py --op rank_share [--workload 4] [--sp 8] [--rank 0]
+    python bench.py --op cat_pad
 
 One step = one jpa_forward_ws call over the whole workload (all query rows of
 all heads, inputs already resident in HBM).  Prints ONE JSON line:
@@ -25,6 +26,9 @@ workload; value is GB/s of algorithmic HBM bytes, roofline against 8 TB/s.
 --op rank_share measures one rank's share of a head-parallel split of the
 attention workload over --sp ranks (Hq/sp and Hkv/sp heads over the whole
 sequence), the replicated prefix read through head-sliced views.
+--op cat_pad measures the fused cat + pad of causal Conv3D caches over the
+eight synthetic decoder shapes (one step = the eight calls); GB/s of
+algorithmic bytes (inputs read once, output written once) against 8 TB/s.
 """
 
 import argparse
@@ -223,13 +227,89 @@ def bench_norm_rope(args):
     print(json.dumps(result), flush=True)
 
 
+CP_METRIC = "causal Conv3D cat+pad GB/s (algorithmic HBM bytes) + % of MI355X HBM peak"
+CP_KERNEL_NAME = "jpa_cat_pad_kernel"
+CP_KERNEL_SOURCES = ("diffusion_transformer_joint_non_amd/csrc/jpa_cat_pad.hip",
+                     "diffusion_transformer_joint_non_amd/csrc/jpa_cat_pad_params.h")
+
+
+def bench_cat_pad(args):
+    """One step = jpa_causal_cat_pad over each of the eight decoder shapes."""
+    import torch
+    import synth
+    from diffusion_transformer_joint_non_amd import jpa
+
+    cases = synth.CAT_PAD_CASES
+    dv = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    data, nbytes = [], 0
+    for c in cases:
+        inp = synth.make_cat_pad_inputs(c)
+        x = dv(inp["x"])
+        cache = dv(inp["cache"]) if c.cache_frames else None
+        out = jpa.jpa_causal_cat_pad(x, cache, c.padding)
+        nbytes += 2 * (x.numel() + (cache.numel() if cache is not None else 0) + out.numel())
+        data.append((c, inp, x, cache, out))
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for c, _, x, cache, out in data:
+            jpa.jpa_causal_cat_pad(x, cache, c.padding, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step_ms = np.asarray([e0.elapsed_time(e1) for e0, e1 in ev])
+    ms_per_step = wall * 1e3 / args.steps
+    kern_ms = float(np.mean(per_step_ms))
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    result = {
+        "metric": CP_METRIC, "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "causal_conv3d_cat_pad_decoder", "shapes": [c.name for c in cases],
+                   "algorithmic_bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": load_traffic("decoder", CP_KERNEL_NAME, CP_KERNEL_SOURCES),
+                     "kernel": CP_KERNEL_NAME,
+                     "kernel_ms_per_step": {"mean": round(kern_ms, 4), "min": round(float(per_step_ms.min()), 4),
+                                            "max": round(float(per_step_ms.max()), 4)},
+                     "kernel_source_sha256_16": kernel_source_hash(CP_KERNEL_SOURCES)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        sub = data[:4]
+        sub_bytes = sum(2 * (x.numel() + (cache.numel() if cache is not None else 0) + out.numel())
+                        for _, _, x, cache, out in sub)
+        t0 = time.perf_counter()
+        refs = [oracle.cat_pad(inp["x"], inp["cache"] if c.cache_frames else None, c.padding)
+                for c, inp, _, _, _ in sub]
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(sub_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle", "seconds": round(dt, 3),
+                                  "sample": "the four smallest shapes: " + ", ".join(c.name for c, *_ in sub)}
+        same = all(np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), r)
+                   for (_, _, _, _, out), r in zip(sub, refs))
+        result["parity"] = {"bit_exact_on_sample": bool(same)}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=None)
-    ap.add_argument("--op", choices=("attention", "norm_rope", "rank_share"), default="attention")
+    ap.add_argument("--op", choices=("attention", "norm_rope", "rank_share", "cat_pad"), default="attention")
     ap.add_argument("--sp", type=int, default=8, help="rank_share: ranks of the head split")
     ap.add_argument("--rank", type=int, default=0, help="rank_share: which rank's share")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -251,6 +331,9 @@ def main():
 
     if args.op == "norm_rope":
         bench_norm_rope(args)
+        return
+    if args.op == "cat_pad":
+        bench_cat_pad(args)
         return
 
     import synth

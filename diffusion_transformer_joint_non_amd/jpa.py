@@ -1,5 +1,6 @@
 """Thin ctypes binding over libjpa's C ABI (include/jpa.h,
-include/jpa_norm_rope.h and include/jpa_shard.h), same names.
+include/jpa_norm_rope.h, include/jpa_shard.h and include/jpa_cat_pad.h), same
+names.
 
 Argument marshalling only: every step of the attention runs in the HIP
 library.  PyTorch supplies device memory and the current stream; nothing else
@@ -30,7 +31,7 @@ BLOCK_M = 256          # query rows per workgroup (for launch accounting only)
 
 EXPORTED = ("jpa_forward", "jpa_forward_ws", "jpa_workspace_bytes", "jpa_validate", "jpa_plan",
             "jpa_status_str", "jpa_abi_version", "jpa_qk_norm_rope", "jpa_shard_plan",
-            "jpa_tail_attn_meta", "jpa_tail_segments")
+            "jpa_tail_attn_meta", "jpa_tail_segments", "jpa_causal_cat_pad")
 
 
 class JpaTensor(ctypes.Structure):
@@ -118,6 +119,8 @@ def load_library() -> ctypes.CDLL:
     lib.jpa_tail_segments.restype = ctypes.c_int
     lib.jpa_tail_segments.argtypes = [sp, ctypes.c_int32, ctypes.c_int32, i32p, ctypes.c_int32, i32p, i32p, i32p]
     vp = ctypes.c_void_p
+    lib.jpa_causal_cat_pad.restype = ctypes.c_int
+    lib.jpa_causal_cat_pad.argtypes = [vp, vp] + [ctypes.c_int32] * 6 + [i32p, vp, vp]
     lib.jpa_qk_norm_rope.restype = ctypes.c_int
     lib.jpa_qk_norm_rope.argtypes = [tp, tp, vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_float, tp, tp, vp]
@@ -360,3 +363,36 @@ def jpa_tail_segments(shard: JpaShard, seqlen_multiplier: int, prefix_lens, quer
                                      _i32p(pl) if b else None, 1 if queries_include_prefix else 0,
                                      _i32p(cu_q), _i32p(cu_p), _i32p(cu_s)))
     return cu_q, cu_p, cu_s
+
+
+def jpa_causal_cat_pad(x, cache, padding, out=None, stream=None):
+    """[cache ; x] along time, zero-padded by padding = (w_left, w_right,
+    h_left, h_right, t_left, t_right).  x [B, C, T, H, W] and cache
+    [B, C, Tc, H, W] (or None): contiguous CUDA tensors with 2-byte elements.
+    Returns out (allocated when None)."""
+    import torch
+    lib = load_library()
+    if x.dim() != 5 or x.element_size() != 2 or not x.is_contiguous():
+        raise JpaArgumentError(JPA_ERR_SHAPE, "x must be a contiguous 5-D tensor of 2-byte elements")
+    b, c, t, h, w = x.shape
+    tc = 0
+    if cache is not None:
+        if (cache.dim() != 5 or cache.dtype != x.dtype or not cache.is_contiguous()
+                or tuple(cache.shape[:2]) != (b, c) or tuple(cache.shape[3:]) != (h, w)):
+            raise JpaArgumentError(JPA_ERR_SHAPE, "cache must be a contiguous [B, C, Tc, H, W] like x")
+        tc = cache.shape[2]
+    pad = _i32(padding)
+    if pad.size != 6:
+        raise JpaArgumentError(JPA_ERR_SHAPE, "padding has six entries")
+    shape = (b, c, tc + t + int(pad[4]) + int(pad[5]), h + int(pad[2]) + int(pad[3]), w + int(pad[0]) + int(pad[1]))
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise JpaArgumentError(JPA_ERR_SHAPE, f"out must be a contiguous {shape} tensor like x")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    ptr = lambda v: ctypes.c_void_p(v.data_ptr()) if v is not None and v.numel() else None
+    st = lib.jpa_causal_cat_pad(ptr(x), ptr(cache), b, c, t, tc, h, w, _i32p(pad), ptr(out), ctypes.c_void_p(handle))
+    _raise_for(st)
+    return out

@@ -366,3 +366,30 @@ def test_norm_rope_valid_calls_reach_the_launch(case):
         q, k, qo, ko = (_nr_tensor(40, h, 64, base=b) for h, b in ((4, _FAKE), (2, 2 * _FAKE), (4, 3 * _FAKE), (2, 4 * _FAKE)))
         kw.update(rot=48, il=1, tstride=48)
     assert _nr_call(q, k, qo, ko, **kw) == jpa.JPA_ERR_HIP
+
+
+# ---------------------------------------------------------------- jpa_causal_cat_pad
+
+def _cp_call(x=_FAKE, cache=2 * _FAKE, dims=(1, 4, 2, 8, 16), tc=2, pad=(1, 1, 1, 1, 0, 0), out=4 * _FAKE):
+    lib = jpa.load_library()
+    b, c, t, h, w = dims
+    p = (ctypes.c_int32 * 6)(*pad)
+    return lib.jpa_causal_cat_pad(ctypes.c_void_p(x) if x else None, ctypes.c_void_p(cache) if cache else None,
+                                  b, c, t, tc, h, w, p, ctypes.c_void_p(out) if out else None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=0), jpa.JPA_ERR_NULL), (dict(x=0), jpa.JPA_ERR_NULL), (dict(cache=0), jpa.JPA_ERR_NULL),
+    (dict(pad=(1, -1, 1, 1, 0, 0)), jpa.JPA_ERR_VALUE), (dict(dims=(1, 4, -2, 8, 16)), jpa.JPA_ERR_SHAPE),
+    (dict(dims=(1, 4, 2, 8, 70000)), jpa.JPA_ERR_SHAPE), (dict(dims=(64, 1024, 64, 256, 256)), jpa.JPA_ERR_SHAPE),
+    (dict(x=_FAKE + 8), jpa.JPA_ERR_LAYOUT), (dict(out=_FAKE + 64), jpa.JPA_ERR_LAYOUT),
+    (dict(out=2 * _FAKE + 32), jpa.JPA_ERR_LAYOUT),
+])
+def test_cat_pad_rejects(kw, code):
+    assert _cp_call(**kw) == code
+
+
+def test_cat_pad_empty_and_uncached():
+    assert _cp_call(dims=(0, 4, 2, 8, 16), x=0, cache=0, out=0) == jpa.JPA_OK
+    if not torch.cuda.is_available():
+        assert _cp_call(cache=0, tc=0) == jpa.JPA_ERR_HIP       # valid call reaches the launch
