@@ -287,19 +287,20 @@ def bench_cat_pad(args):
     }
     if not args.no_cpu_baseline:
         import oracle
-        sub = data[:4]
+        sub = data
         sub_bytes = sum(2 * (x.numel() + (cache.numel() if cache is not None else 0) + out.numel())
                         for _, _, x, cache, out in sub)
         t0 = time.perf_counter()
-        refs = [oracle.cat_pad(inp["x"], inp["cache"] if c.cache_frames else None, c.padding)
-                for c, inp, _, _, _ in sub]
+        same = True
+        for c, inp, _, _, out in sub:
+            ref = oracle.cat_pad(inp["x"], inp["cache"] if c.cache_frames else None, c.padding)
+            same &= bool(np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), ref))
+            del ref
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(sub_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
                                   "kind": "oracle", "seconds": round(dt, 3),
-                                  "sample": "the four smallest shapes: " + ", ".join(c.name for c, *_ in sub)}
-        same = all(np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), r)
-                   for (_, _, _, _, out), r in zip(sub, refs))
-        result["parity"] = {"bit_exact_on_sample": bool(same)}
+                                  "sample": "all eight shapes (time includes the bitwise comparison)"}
+        result["parity"] = {"bit_exact": bool(same)}
     print(json.dumps(result), flush=True)
 
 
