@@ -402,6 +402,12 @@ def main():
     kern_ms = float(np.mean(per_launch_ms))
     achieved = flops / (kern_ms * 1e-3) / 1e12
     traffic = load_traffic(w.name)
+    # minimum bytes a call moves: real q read, every out slot written, each
+    # row's real prefix/suffix K and V read once, lse written
+    real_q = int(sum(r[2] for r in rows))
+    real_kv = int(sum(r[8] for r in rows))
+    algo_bytes = (2 * w.d * w.hq * (real_q + int(x["cu_q"][-1])) + 2 * 2 * w.d * w.hkv * real_kv
+                  + 4 * w.hq * int(x["cu_q"][-1]))
 
     result = {
         "metric": METRIC,
@@ -429,7 +435,10 @@ def main():
                                    "median": round(float(np.median(per_launch_ms)), 4),
                                    "min": round(float(per_launch_ms.min()), 4),
                                    "max": round(float(per_launch_ms.max()), 4)},
-                     "kernel_source_sha256_16": kernel_source_hash()},
+                     "kernel_source_sha256_16": kernel_source_hash(),
+                     "algorithmic_bytes": algo_bytes,
+                     "hbm_gbs_algorithmic": round(algo_bytes / (kern_ms * 1e-3) / 1e9, 1),
+                     "us_per_call": round(kern_ms * 1e3, 2)},
     }
 
     if not args.no_cpu_baseline:
