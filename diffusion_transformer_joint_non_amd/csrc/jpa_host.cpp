@@ -109,6 +109,8 @@ jpa_status device_cus(int* cus) {
 // tiles, an all-pad item 1.  Whole rounds of wgs items run one item per
 // workgroup; the items of the last, partial round are cut into wgs balanced
 // ranges of key tiles, whose cut items a second kernel merges.
+constexpr int kMinTilesPerRange = 8;
+
 void plan_split(jpa_kernel_params& p, int wgs, bool forced, char* ws, int head_dim) {
     const int64_t items = (int64_t)p.total_tiles * p.hq;
     int64_t head_units = 0;
@@ -138,6 +140,9 @@ void plan_split(jpa_kernel_params& p, int wgs, bool forced, char* ws, int head_d
         const int64_t u = tile_units[it % p.total_tiles];
         if (it < n_dp) unit0 += u; else tail += u;
     }
+    // ... and only when every range gets enough key tiles to amortise its
+    // pieces' prologues and the merge launch (tiny problems stay uncut)
+    if (!forced && tail < (int64_t)kMinTilesPerRange * wgs) return;
     p.n_dp = (int32_t)n_dp;
     p.sk_wgs = (int32_t)std::min<int64_t>(wgs, tail);
     p.tail_unit0 = unit0;

@@ -173,7 +173,8 @@ JPA_API jpa_status jpa_forward(const jpa_tensor* q,
  *   workspace_bytes  its size; a smaller size than required is JPA_ERR_VALUE.
  *   split_wgs        0: ranges = compute units, and the last round is cut
  *                    only when it would leave more than half of them idle
- *                    (each cut piece pays a prologue and a merge); > 0: that
+ *                    and every range gets at least 8 key tiles (each cut
+ *                    piece pays a prologue and a merge); > 0: that
  *                    many ranges, always cut (a tuning and testing knob).
  * Errors as jpa_forward, plus JPA_ERR_LAYOUT for a misaligned workspace and
  * JPA_ERR_HIP when the device cannot be queried.
