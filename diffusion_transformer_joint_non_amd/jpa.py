@@ -215,8 +215,9 @@ _workspaces = {}
 
 
 def workspace_for(device, stream_handle: int, head_dim: int = 128, split_wgs: int = 0):
-    """A zero-filled workspace for jpa_forward_ws, cached per (device, stream,
-    split_wgs): calls on one stream are ordered, so they may share it."""
+    """A workspace for jpa_forward_ws, cached per (device, stream, split_wgs,
+    head_dim): calls on one stream are ordered, so they may share it (its
+    contents do not matter between calls)."""
     import torch
     dev = torch.device(device)
     key = (dev.index, int(stream_handle), int(split_wgs), int(head_dim))
@@ -225,7 +226,7 @@ def workspace_for(device, stream_handle: int, head_dim: int = 128, split_wgs: in
         n = jpa_workspace_bytes(head_dim, split_wgs)
         if n == 0:
             raise JpaError(JPA_ERR_HIP, "cannot size the workspace for this device")
-        ws = torch.zeros(n, dtype=torch.uint8, device=dev)
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
@@ -249,9 +250,9 @@ def jpa_forward_ws(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix, c
                    scale: float, out=None, lse=None, stream=None, with_lse: bool = True,
                    workspace="auto", split_wgs: int = 0):
     """jpa_forward with a workspace that balances the last round of work over
-    every compute unit.  ``workspace``: "auto" (a cached zero-filled buffer
+    every compute unit.  ``workspace``: "auto" (a cached buffer
     per device and stream), a uint8 CUDA tensor of at least
-    jpa_workspace_bytes() bytes whose counters are zero, or None (then the
+    jpa_workspace_bytes() bytes (contents do not matter), or None (then the
     call is jpa_forward's).  Returns (out, lse)."""
     lib = load_library()
     cq, cp, cs, batch, d = _common(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix,
