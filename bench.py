@@ -12,8 +12,10 @@ all heads, inputs already resident in HBM).  Prints ONE JSON line:
 
 * value / ms_per_step: valid-token TFLOP/s of the timed steps
   (FLOPs = sum_b Hq * 4 * D * Nq_b * Nk_b, from jpa_plan);
-* roofline: the kernel's per-launch duration from HIP events recorded on the
-  stream it is launched on, against the bf16 dense MFMA peak;
+* roofline: the kernel's GPU time per launch from HIP events recorded on the
+  launch stream at the two ends of the timed region (nothing is inserted
+  between launches), against the bf16 dense MFMA peak; a separate pass with
+  an event pair around each launch gives the per-launch spread;
 * cpu_baseline: the fp64 oracle timed on this host's cores;
 * parity: the GPU result of the timed call against that oracle run.
 
@@ -82,6 +84,35 @@ def load_traffic(workload_name: str, kernel=KERNEL_NAME, sources=KERNEL_SOURCES)
     if rec.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def timed_steps(step, steps: int, stream):
+    """Time `steps` calls of step(): the wall clock between two synchronise
+    barriers, and HIP events recorded on the launch stream at the two ends of
+    the same region (the region's GPU time per step; no event sits between
+    the steps, so nothing is inserted between back-to-back launches).  Then a
+    separate pass with an event pair around every step gives per-launch
+    spread.  Returns (wall ms/step, event ms/step, per-launch ms array)."""
+    import torch
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    region_ms = e0.elapsed_time(e1) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(min(steps, 10))]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = np.asarray([a.elapsed_time(b) for a, b in ev])
+    return wall_ms, region_ms, per
 
 
 def blas_threads() -> int:
@@ -173,18 +204,7 @@ def bench_norm_rope(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch_ms = np.asarray([e0.elapsed_time(e1) for e0, e1 in ev])
-    ms_per_step = wall * 1e3 / args.steps
-    kern_ms = float(np.mean(per_launch_ms))
+    ms_per_step, kern_ms, per_launch_ms = timed_steps(step, args.steps, stream)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     result = {
         "metric": NR_METRIC,
@@ -201,9 +221,9 @@ def bench_norm_rope(args):
                      "traffic": load_traffic(w.name, NR_KERNEL_NAME, NR_KERNEL_SOURCES),
                      "kernel": NR_KERNEL_NAME,
                      "kernel_ms": {"mean": round(kern_ms, 4),
-                                   "median": round(float(np.median(per_launch_ms)), 4),
-                                   "min": round(float(per_launch_ms.min()), 4),
-                                   "max": round(float(per_launch_ms.max()), 4)},
+                                   "per_launch_pass": {"median": round(float(np.median(per_launch_ms)), 4),
+                                                       "min": round(float(per_launch_ms.min()), 4),
+                                                       "max": round(float(per_launch_ms.max()), 4)}},
                      "kernel_source_sha256_16": kernel_source_hash(NR_KERNEL_SOURCES)},
     }
     if not args.no_cpu_baseline:
@@ -258,18 +278,7 @@ def bench_cat_pad(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_step_ms = np.asarray([e0.elapsed_time(e1) for e0, e1 in ev])
-    ms_per_step = wall * 1e3 / args.steps
-    kern_ms = float(np.mean(per_step_ms))
+    ms_per_step, kern_ms, per_step_ms = timed_steps(step, args.steps, stream)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     result = {
         "metric": CP_METRIC, "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s",
@@ -281,8 +290,9 @@ def bench_cat_pad(args):
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": load_traffic("decoder", CP_KERNEL_NAME, CP_KERNEL_SOURCES),
                      "kernel": CP_KERNEL_NAME,
-                     "kernel_ms_per_step": {"mean": round(kern_ms, 4), "min": round(float(per_step_ms.min()), 4),
-                                            "max": round(float(per_step_ms.max()), 4)},
+                     "kernel_ms_per_step": {"mean": round(kern_ms, 4),
+                                            "per_step_pass": {"min": round(float(per_step_ms.min()), 4),
+                                                              "max": round(float(per_step_ms.max()), 4)}},
                      "kernel_source_sha256_16": kernel_source_hash(CP_KERNEL_SOURCES)},
     }
     if not args.no_cpu_baseline:
@@ -383,25 +393,37 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Per-launch events on the launch stream give the kernel's own duration;
-    # the synchronised wall clock around all K steps gives ms_per_step.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # HIP events on the launch stream at the two ends of the timed region give
+    # the GPU time per launch; the synchronised wall clock gives ms_per_step.
     log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch_ms = np.asarray([e0.elapsed_time(e1) for e0, e1 in ev])
-    ms_per_step = wall * 1e3 / args.steps
-
-    kern_ms = float(np.mean(per_launch_ms))
+    ms_per_step, kern_ms, per_launch_ms = timed_steps(step, args.steps, stream)
     achieved = flops / (kern_ms * 1e-3) / 1e12
     traffic = load_traffic(w.name)
+    # Launch-bound sizes: the per-call time when the host is out of the way,
+    # from a HIP graph of 20 calls replayed (the library allocates nothing and
+    # never synchronises, so its calls capture as they are).
+    graph_us = None
+    if kern_ms < 1.0:
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                for _ in range(20):
+                    jpa.jpa_forward_ws(dev["q"], dev["k_prefix"], dev["v_prefix"], dev["k_suffix"],
+                                       dev["v_suffix"], x["cu_q"], x["cu_prefix"], x["cu_suffix_real"],
+                                       x["scale"], out=out, lse=lse, stream=cs,
+                                       workspace=jpa.workspace_for(out.device, stream.cuda_stream, w.d))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(5):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_us = g0.elapsed_time(g1) * 1e3 / (5 * 20)
     # minimum bytes a call moves: real q read, every out slot written, each
     # row's real prefix/suffix K and V read once, lse written
     real_q = int(sum(r[2] for r in rows))
@@ -432,13 +454,14 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": KERNEL_NAME,
                      "kernel_ms": {"mean": round(kern_ms, 4),
-                                   "median": round(float(np.median(per_launch_ms)), 4),
-                                   "min": round(float(per_launch_ms.min()), 4),
-                                   "max": round(float(per_launch_ms.max()), 4)},
+                                   "per_launch_pass": {"median": round(float(np.median(per_launch_ms)), 4),
+                                                       "min": round(float(per_launch_ms.min()), 4),
+                                                       "max": round(float(per_launch_ms.max()), 4)}},
                      "kernel_source_sha256_16": kernel_source_hash(),
                      "algorithmic_bytes": algo_bytes,
                      "hbm_gbs_algorithmic": round(algo_bytes / (kern_ms * 1e-3) / 1e9, 1),
-                     "us_per_call": round(kern_ms * 1e3, 2)},
+                     "us_per_call": round(kern_ms * 1e3, 2),
+                     "us_per_call_graph": None if graph_us is None else round(graph_us, 2)},
     }
 
     if not args.no_cpu_baseline:
