@@ -227,3 +227,43 @@ def test_empty_batch_and_empty_rows():
     out, lse = jpa.jpa_forward(z, z, z, z, z, [0], [0], [0], 0.125)
     torch.cuda.synchronize()
     assert out.shape[0] == 0 and lse.shape == (2, 0)
+
+
+def _random_case(seed):
+    """A seeded random layout: 1-5 rows, prefix / real suffix / pad lengths
+    from empty to a few tiles (ragged), GQA group 1-4, D 64 or 128, queries
+    over the suffix or over prefix + suffix.  Rows with real queries always
+    get at least one key."""
+    rng = np.random.default_rng(seed)
+    b = int(rng.integers(1, 6))
+    hkv = int(rng.integers(1, 4))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    prefix = [int(v) for v in rng.integers(0, 700, b)]
+    real = [int(v) for v in rng.integers(0, 900, b)]
+    pad = [int(v) for v in rng.integers(0, 300, b)]
+    queries = "prefix+suffix" if rng.random() < 0.5 else "suffix"
+    for i in range(b):
+        if prefix[i] + real[i] == 0:
+            real[i] = 1
+    return synth.custom_workload(hq, hkv, d, prefix, real, pad, queries, wid=500 + seed)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_parity_random_layouts(seed):
+    w = _random_case(seed)
+    x = synth.make_inputs(w, pad_fill="garbage")
+    _say(f"random layout {seed}: hq={w.hq} hkv={w.hkv} d={w.d} P={w.prefix} R={w.suffix_real} "
+         f"pad={w.suffix_pad} q={w.queries}")
+    for split in (None, 16):
+        dev = gh.device_inputs(x)
+        if split is None:
+            o, l = gh.run(x, dev)
+        else:
+            o, l = jpa.jpa_forward_ws(dev["q"], dev["k_prefix"], dev["v_prefix"], dev["k_suffix"],
+                                      dev["v_suffix"], x["cu_q"], x["cu_prefix"], x["cu_suffix_real"],
+                                      x["scale"], split_wgs=split)
+            torch.cuda.synchronize()
+        out, lse = gh.host(o, l)
+        gh.assert_parity_full(w, x, out, lse)
+        gh.assert_pad_rows(w, out, lse)
