@@ -8,21 +8,31 @@
 //   src = [cache ; x] along time (cache frames first).
 //
 // Pure data movement, bound by HBM.  Design:
-// * one thread writes one aligned 16-byte chunk (8 elements) of the flat
+// * one thread owns one aligned 16-byte chunk (8 elements) of the flat
 //   output; it finds the chunk's row (b, c, t, h) with multiply-shift
 //   divisions (constants from the host) and its first column;
 // * a chunk inside one output row whose 8 source elements all exist reads
 //   two aligned 16-byte source chunks and shifts them into place
 //   (v_alignbyte_b32), so a row shifted by the left pad is still read with
-//   16-byte loads; chunks at row edges or running into the next row go
-//   element by element with each row's source located once (no division per
-//   element); pad elements are zeros without any load;
+//   16-byte loads; a chunk of zeros (a padded row, a run of pad columns)
+//   loads nothing;
 // * the upper aligned source chunk of a shifted read is, for consecutive
 //   chunks of one row, the lower chunk of the next lane: it comes from that
 //   lane by a DPP wave shift (checked by an address tag), so a shifted row
 //   costs one 16-byte load per chunk, not two;
-// * each thread handles kChunks chunks spaced a grid apart, loads first, so
-//   several 16-byte loads per lane are in flight.
+// * every other chunk (a row edge with pad columns, a chunk across two rows,
+//   the tensor's last chunk) is an edge chunk: the wave collects its edge
+//   chunks by ballot and writes them with all 64 lanes at once, eight lanes
+//   per chunk, one element per lane, so a row edge does not hold the rest of
+//   the wave on an element-by-element path;
+// * a lane's loads (lower chunk, own upper chunk, edge element) are all
+//   issued before any is waited for: whether the upper chunk comes from the
+//   neighbour follows from the two lanes' plans, not from loaded data;
+// * the tensor pointers live in scalar registers: a per-lane choice between
+//   two kernel arguments compiles to a per-lane load of the argument block,
+//   which had cost a dependent memory round trip per chunk;
+// * one chunk per thread and up to 32 workgroups per CU measured best
+//   (kChunks chunks spaced a grid apart are supported).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -34,7 +44,7 @@ namespace {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kChunks = 2;
+constexpr int kChunks = 1;
 
 __device__ __forceinline__ uint32_t divm(uint32_t n, uint32_t magic, int shift) {
     return (uint32_t)(((uint64_t)n * magic) >> shift);
@@ -57,127 +67,171 @@ __device__ __forceinline__ int32_t source_row(const jpa_cat_pad_params& p, uint3
     return (int32_t)(((n * frames + ts) * (uint32_t)p.height + (uint32_t)hh) * (uint32_t)p.width);
 }
 
-// The 8 elements from flat source index s0 (any alignment) with two aligned
-// 16-byte loads and a byte shift; a + 16 elements must lie inside src.
-__device__ __forceinline__ u32x4_t load8_shifted(const uint16_t* src, uint32_t s0) {
-    const uint32_t a = s0 & ~7u;
-    const uint32_t off = s0 - a;
-    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(src + a);
-    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(src + a + 8);
-    const uint32_t d[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    const uint32_t k = off >> 1;                       // first dword, then a 2-byte shift if off is odd
-    uint32_t wv[5];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        const uint32_t lo2 = (k & 1) ? d[i + 1] : d[i];
-        const uint32_t hi2 = (k & 1) ? d[i + 3] : d[i + 2];
-        wv[i] = (k & 2) ? hi2 : lo2;
-    }
-    const uint32_t sh = (off & 1) * 2;
-    u32x4_t r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_alignbyte(wv[i + 1], wv[i], sh);
-    return r;
+// A wave-uniform 64-bit value held in scalar registers.  Per-lane choices
+// between two kernel arguments (x or cache) are made on such copies: a
+// choice between the arguments themselves compiles to a per-lane load from
+// the argument block.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
-// One 16-byte output chunk at flat element o.  Lanes of a wave hold
-// consecutive chunks, so the upper aligned source chunk a lane needs is
-// usually the lower one its right neighbour loads: it is taken from that
-// lane (DPP wave shift) and loaded only where the neighbour's differs.
-__device__ __forceinline__ u32x4_t chunk_value(const jpa_cat_pad_params& p, uint32_t o, bool live) {
+// Global-memory views (address space 1), so loads stay global loads.
+typedef const __attribute__((address_space(1))) uint16_t g_u16;
+typedef const __attribute__((address_space(1))) u32x4_t g_u32x4;
+
+// The two source tensors as such scalar copies.
+struct sources {
+    g_u16* x;
+    g_u16* cache;
+    int64_t x_numel, cache_numel;
+};
+
+// How the 16-byte output chunk at flat element o is written.  "data": the
+// chunk lies inside one output row and holds 8 source elements of one source
+// row, read as the aligned source chunk at a (plus the next one when off,
+// the misalignment, is not 0).  "zero": inside one row and all padding (a
+// padded row, a run of pad columns).  Anything else -- a row edge with pad
+// columns, a chunk across two rows, a shifted read at a tensor's last chunk
+// -- is an edge chunk.  No memory is touched.
+struct chunk_plan {
+    g_u16* src;
+    uint32_t a, off, tag;    // tag: a | tensor bit for data chunks, else ~0
+    bool data, edge;
+};
+
+__device__ __forceinline__ chunk_plan plan_chunk(const jpa_cat_pad_params& p, const sources& sv, uint32_t o,
+                                                 bool live) {
     const uint32_t row = divm(o, p.w_magic, p.w_shift);
     const int col = (int)(o - row * (uint32_t)p.w_out);
-    bool c0 = false, c1 = false;
-    const int32_t b0 = live ? source_row(p, row, &c0) : -1;
+    const bool in_row = live && col + 8 <= p.w_out;   // then o + 8 <= out_numel
+    bool c0 = false;
+    const int32_t b0 = in_row ? source_row(p, row, &c0) : -1;
     const int w0 = col - p.pad_w0;                     // source column of element 0
-    const bool fast = b0 >= 0 && w0 >= 0 && w0 + 8 <= p.width;
-    const uint16_t* src = c0 ? p.cache : p.x;
-    const uint32_t s0 = fast ? (uint32_t)b0 + (uint32_t)w0 : 0u;
-    const uint32_t a = s0 & ~7u;
-    u32x4_t lo = u32x4_t{0u, 0u, 0u, 0u};
-    if (fast) lo = *reinterpret_cast<const u32x4_t*>(src + a);
-    // the right neighbour's lower chunk and its address tag (every lane runs the shifts)
-    const uint32_t tag = fast ? (a | (c0 ? 1u : 0u)) : 0xFFFFFFFFu;
-    const uint32_t ntag = (uint32_t)__builtin_amdgcn_mov_dpp((int)tag, 0x130, 0xF, 0xF, false);   // wave_shl:1
-    u32x4_t hi;
+    const bool zero = in_row && (b0 < 0 || w0 + 8 <= 0 || w0 >= p.width);
+    const uint32_t s0 = (uint32_t)b0 + (uint32_t)w0;
+    chunk_plan pl;
+    pl.src = c0 ? sv.cache : sv.x;
+    pl.a = s0 & ~7u;
+    pl.off = s0 - pl.a;
+    const int64_t numel = c0 ? sv.cache_numel : sv.x_numel;
+    pl.data = b0 >= 0 && w0 >= 0 && w0 + 8 <= p.width && (pl.off == 0 || (int64_t)pl.a + 16 <= numel);
+    pl.edge = live && !pl.data && !zero;
+    pl.tag = pl.data ? (pl.a | (c0 ? 1u : 0u)) : 0xFFFFFFFFu;
+    return pl;
+}
+
+// Output element o (< out_numel), located on its own.
+__device__ __forceinline__ uint16_t element_value(const jpa_cat_pad_params& p, const sources& sv, uint32_t o) {
+    const uint32_t row = divm(o, p.w_magic, p.w_shift);
+    const int w = (int)(o - row * (uint32_t)p.w_out) - p.pad_w0;
+    bool c = false;
+    const int32_t base = source_row(p, row, &c);
+    return (base >= 0 && w >= 0 && w < p.width) ? (c ? sv.cache : sv.x)[base + w] : (uint16_t)0;
+}
+
+// Edge chunks are written by the whole wave at once, eight at a time: lane l
+// takes element l % 8 of the (l / 8)-th lowest remaining bit of m (a wave
+// ballot, bit = lane of the chunk), so eight lanes write one chunk's 16
+// contiguous bytes.  Removes those bits from m; returns this lane's chunk
+// lane, or -1.  m is wave-uniform, so is the loop.
+__device__ __forceinline__ int take_eight(uint64_t& m) {
+    const int lane = threadIdx.x & 63;
+    int mine = -1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hi[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo[i], 0x130, 0xF, 0xF, false);
-    if (fast) {
-        const uint32_t off = s0 - a;
-        if (off == 0) return lo;
-        const int64_t numel = c0 ? p.cache_numel : p.x_numel;
-        const bool shared = (threadIdx.x & 63) != 63 && ntag == ((a + 8) | (c0 ? 1u : 0u));
-        if (shared || (int64_t)a + 16 <= numel) {
-            if (!shared) hi = *reinterpret_cast<const u32x4_t*>(src + a + 8);
-            const uint32_t d[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const uint32_t k = off >> 1;
-            uint32_t wv[5];
-#pragma unroll
-            for (int i = 0; i < 5; ++i) {
-                const uint32_t l2 = (k & 1) ? d[i + 1] : d[i];
-                const uint32_t h2 = (k & 1) ? d[i + 3] : d[i + 2];
-                wv[i] = (k & 2) ? h2 : l2;
-            }
-            const uint32_t sh = (off & 1) * 2;
-            u32x4_t r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_alignbyte(wv[i + 1], wv[i], sh);
-            return r;
+    for (int k = 0; k < 8; ++k) {
+        if (m) {
+            const int pos = __builtin_ctzll(m);
+            m &= m - 1;
+            if ((lane >> 3) == k) mine = pos;
         }
     }
-    uint16_t e[8];
-    if (p.w_out >= 8) {
-        const int32_t b1 = live && col + 8 > p.w_out ? source_row(p, row + 1, &c1) : -1;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            e[j] = 0;
-            const bool next = col + j >= p.w_out;
-            const int32_t base = next ? b1 : b0;
-            const int w = (next ? col + j - p.w_out : col + j) - p.pad_w0;
-            if (live && o + j < p.out_numel && base >= 0 && w >= 0 && w < p.width)
-                e[j] = ((next ? c1 : c0) ? p.cache : p.x)[base + w];
-        }
-    } else {
-        for (int j = 0; j < 8; ++j) {
-            e[j] = 0;
-            const uint32_t oj = o + j;
-            if (!live || oj >= p.out_numel) continue;
-            const uint32_t rj = divm(oj, p.w_magic, p.w_shift);
-            const int w = (int)(oj - rj * (uint32_t)p.w_out) - p.pad_w0;
-            bool cj = false;
-            const int32_t base = source_row(p, rj, &cj);
-            if (base >= 0 && w >= 0 && w < p.width) e[j] = (cj ? p.cache : p.x)[base + w];
-        }
-    }
-    u32x4_t r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
-    return r;
+    return mine;
 }
 
 __global__ __launch_bounds__(kThreads) void jpa_cat_pad_kernel(const jpa_cat_pad_params p) {
+    const sources sv = {(g_u16*)uniform64(reinterpret_cast<uintptr_t>(p.x)),
+                        (g_u16*)uniform64(reinterpret_cast<uintptr_t>(p.cache)),
+                        (int64_t)uniform64((uint64_t)p.x_numel), (int64_t)uniform64((uint64_t)p.cache_numel)};
     // chunk c0 + u * stride (u < kChunks) of a pass: every pass tiles
-    // stride * kChunks consecutive chunks, each u-slice of it over the grid
+    // stride * kChunks consecutive chunks, each u-slice of it over the grid;
+    // a wave holds 64 consecutive chunks of each slice and stays in the loop
+    // as a whole (the condition is the same for all its lanes)
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-    for (uint64_t c0 = (uint64_t)blockIdx.x * kThreads + threadIdx.x; c0 < p.chunks; c0 += stride * kChunks) {
-        u32x4_t val[kChunks];
+    const uint64_t lane = threadIdx.x & 63;
+    for (uint64_t c0 = (uint64_t)blockIdx.x * kThreads + threadIdx.x; c0 - lane < p.chunks; c0 += stride * kChunks) {
+        chunk_plan pl[kChunks];
 #pragma unroll
         for (int u = 0; u < kChunks; ++u) {
             const uint64_t chunk = c0 + (uint64_t)u * stride;
-            // every lane calls it (the wave shift needs all lanes), dead ones idle
-            val[u] = chunk_value(p, (uint32_t)(chunk < p.chunks ? chunk * 8 : 0), chunk < p.chunks);
+            pl[u] = plan_chunk(p, sv, (uint32_t)(chunk < p.chunks ? chunk * 8 : 0), chunk < p.chunks);
+        }
+        // the first eight edge chunks of each slice: their loads go out with the others
+        uint64_t em[kChunks];
+        int mine[kChunks];
+        uint16_t ev[kChunks];
+#pragma unroll
+        for (int u = 0; u < kChunks; ++u) {
+            em[u] = __builtin_amdgcn_ballot_w64(pl[u].edge);
+            mine[u] = take_eight(em[u]);
+            const uint64_t o = (c0 - lane + (uint64_t)u * stride + (uint64_t)mine[u]) * 8 + (lane & 7);
+            if (mine[u] < 0 || o >= p.out_numel) mine[u] = -1;
+            ev[u] = mine[u] >= 0 ? element_value(p, sv, (uint32_t)o) : (uint16_t)0;
+        }
+        // whether a lane's upper source chunk is its right neighbour's lower one
+        // follows from the plans alone (address tags by DPP wave shift), so
+        // every load of the pass is issued before any is waited for
+        bool own_hi[kChunks];
+#pragma unroll
+        for (int u = 0; u < kChunks; ++u) {
+            const uint32_t ntag = (uint32_t)__builtin_amdgcn_mov_dpp((int)pl[u].tag, 0x130, 0xF, 0xF, false);  // wave_shl:1
+            own_hi[u] = pl[u].data && pl[u].off != 0 && !(lane != 63 && ntag == pl[u].tag + 8);
+        }
+        u32x4_t lo[kChunks], hi[kChunks];
+#pragma unroll
+        for (int u = 0; u < kChunks; ++u) {
+            lo[u] = u32x4_t{0u, 0u, 0u, 0u};
+            if (pl[u].data) lo[u] = *reinterpret_cast<g_u32x4*>(pl[u].src + pl[u].a);
+            if (own_hi[u]) hi[u] = *reinterpret_cast<g_u32x4*>(pl[u].src + pl[u].a + 8);
+        }
+#pragma unroll
+        for (int u = 0; u < kChunks; ++u) {
+            u32x4_t nb;                                    // the right neighbour's lower chunk
+#pragma unroll
+            for (int i = 0; i < 4; ++i) nb[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo[u][i], 0x130, 0xF, 0xF, false);
+            if (!own_hi[u]) hi[u] = nb;
         }
 #pragma unroll
         for (int u = 0; u < kChunks; ++u) {
             const uint64_t chunk = c0 + (uint64_t)u * stride;
-            if (chunk >= p.chunks) continue;
-            const uint32_t o = (uint32_t)(chunk * 8);      // out_numel < 2^31
-            if (o + 8 <= p.out_numel) {
-                *reinterpret_cast<u32x4_t*>(p.out + o) = val[u];
-            } else {
+            u32x4_t val = lo[u];
+            if (pl[u].off != 0) {                          // shift (data chunks; the rest store lo = 0)
+                const uint32_t d[8] = {lo[u][0], lo[u][1], lo[u][2], lo[u][3], hi[u][0], hi[u][1], hi[u][2], hi[u][3]};
+                const uint32_t k = pl[u].off >> 1;      // first dword, then a 2-byte shift if off is odd
+                uint32_t wv[5];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (o + j < p.out_numel) p.out[o + j] = (uint16_t)(val[u][j >> 1] >> (16 * (j & 1)));
+                for (int i = 0; i < 5; ++i) {
+                    const uint32_t l2 = (k & 1) ? d[i + 1] : d[i];
+                    const uint32_t h2 = (k & 1) ? d[i + 3] : d[i + 2];
+                    wv[i] = (k & 2) ? h2 : l2;
+                }
+                const uint32_t sh = (pl[u].off & 1) * 2;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) val[i] = __builtin_amdgcn_alignbyte(wv[i + 1], wv[i], sh);
+            }
+            if (!pl[u].data) val = u32x4_t{0u, 0u, 0u, 0u};
+            if (chunk < p.chunks && !pl[u].edge)          // a whole in-row chunk: o + 8 <= out_numel
+                *reinterpret_cast<u32x4_t*>(p.out + chunk * 8) = val;
+        }
+#pragma unroll
+        for (int u = 0; u < kChunks; ++u) {
+            const uint64_t base = c0 - lane + (uint64_t)u * stride;
+            if (mine[u] >= 0) p.out[(base + (uint64_t)mine[u]) * 8 + (lane & 7)] = ev[u];
+            while (em[u]) {                                // more than eight edge chunks in the slice
+                const int more = take_eight(em[u]);
+                const uint64_t o = (base + (uint64_t)more) * 8 + (lane & 7);
+                if (more >= 0 && o < p.out_numel) p.out[o] = element_value(p, sv, (uint32_t)o);
             }
         }
     }
@@ -193,7 +247,7 @@ int jpa_launch_cat_pad(const jpa_cat_pad_params& p, void* stream) {
         cus = 256;
     const uint64_t per_block = (uint64_t)kThreads * kChunks;
     const uint64_t blocks = (p.chunks + per_block - 1) / per_block;
-    const uint64_t cap = (uint64_t)(cus > 0 ? cus : 256) * 16;
+    const uint64_t cap = (uint64_t)(cus > 0 ? cus : 256) * 32;
     const int grid = (int)(blocks < cap ? blocks : cap);
     hipLaunchKernelGGL(jpa_cat_pad_kernel, dim3(grid), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream), p);
     return (int)hipGetLastError();

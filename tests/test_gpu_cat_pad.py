@@ -2,8 +2,9 @@
 cat + pad oracle: bit for bit, on shapes chosen to exercise every path (16-
 byte aligned rows, rows shifted by odd and even left pads, chunks crossing
 rows, rows narrower than a chunk, a ragged final chunk, no cache, no frames,
-no padding), and on the eight synthetic decoder shapes at full size with the
-oracle on two channels (channels are independent)."""
+no padding), on seeded random small shapes, and on the eight synthetic
+decoder shapes at full size with the oracle on two channels (channels are
+independent)."""
 
 import numpy as np
 import pytest
@@ -53,6 +54,28 @@ def test_bit_exact_small(case):
     ref = oracle.cat_pad(x, cache, pad)
     assert tuple(out.shape) == ref.shape
     assert np.array_equal(_host_bits(out), ref)
+
+
+def _random_case(seed):
+    r = np.random.default_rng(1000 + seed)
+    b, c, t, h = (int(v) for v in (r.integers(1, 3), r.integers(1, 6), r.integers(0, 4), r.integers(1, 12)))
+    w, tc = int(r.integers(1, 70)), int(r.integers(0, 3))
+    pad = tuple(int(v) for v in r.integers(0, 4, 6))
+    if t + tc == 0:
+        t = 1
+    return b, c, t, h, w, tc, pad
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_bit_exact_random(seed):
+    """Seeded random shapes and pads: rows of every width against the chunk
+    size, so that waves mix in-row chunks, row edges and multi-row chunks."""
+    b, c, t, h, w, tc, pad = _random_case(seed)
+    x = _rand((b, c, t, h, w), 10 + seed)
+    cache = _rand((b, c, tc, h, w), 50 + seed) if tc else None
+    out = jpa.jpa_causal_cat_pad(_dev(x), None if cache is None else _dev(cache), pad)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host_bits(out), oracle.cat_pad(x, cache, pad))
 
 
 @pytest.mark.parametrize("case", synth.CAT_PAD_CASES, ids=[c.name for c in synth.CAT_PAD_CASES])
