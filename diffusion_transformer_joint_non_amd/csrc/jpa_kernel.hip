@@ -21,8 +21,7 @@
 // * K and V tiles are copied global -> LDS by direct-to-LDS loads (16 bytes
 //   per lane, no staging registers) into natural [key][d] tiles; the V^T
 //   operand is read with the gfx950 LDS transpose load ds_read_b64_tr_b16.
-//   XOR swizzles of the 16-byte (K) and 8-byte (V) chunks keep the reads free
-//   of bank conflicts.  Four K and four V tile buffers, each its own LDS
+//   XOR swizzles of the 16-byte chunks keep the reads free of bank conflicts.  Four K and four V tile buffers, each its own LDS
 //   array: tile t+3 is fetched while tile t is computed (its loads issued
 //   from the MFMA slots), and the per-tile barrier only waits for the copy
 //   issued one tile earlier.
@@ -92,6 +91,25 @@ __device__ __forceinline__ int perm_k(int i) {
 // of a half get 0..15, distinct modulo 8 within each group of 8 lanes.
 __device__ __forceinline__ int swz_k(int row) {
     return (row & 3) | (((row >> 3) & 1) << 2) | (((row >> 2) & 1) << 3);
+}
+
+// V tiles: the 16-byte chunk c of key row r sits at chunk v_pos(c, r) of
+// its LDS row.  The row term spreads the four rows one transposed read
+// touches; for D = 128 the second term also sends the upper 16 features of
+// each 32-feature block to the other half of the 256-byte row, so the 32
+// lanes an LDS cycle serves hit 32 different 8-byte bank pairs.  Both terms
+// are XORs, so the inverse (the chunk a DMA lane fetches for position p) is
+// v_chunk_at(p, r).
+template <int D>
+__device__ __forceinline__ int v_pos(int c, int r) {
+    const int kc = D / 8;
+    return ((D == 128 ? (c ^ (((c >> 1) & 1) << 3)) : c) ^ (2 * (r & 3))) & (kc - 1);
+}
+template <int D>
+__device__ __forceinline__ int v_chunk_at(int p, int r) {
+    const int kc = D / 8;
+    const int x = (p ^ (2 * (r & 3))) & (kc - 1);
+    return D == 128 ? (x ^ (((x >> 1) & 1) << 3)) : x;
 }
 
 __device__ __forceinline__ float other_half_max(float x) {
@@ -417,7 +435,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         const uint16_t* gk = pre ? kp + tp * kp_ts : ks + ts * ks_ts;
         const uint16_t* gv = pre ? vp + tp * vp_ts : vs + ts * vs_ts;
         lds_copy16(gk + ((pc ^ swz_k(row)) & (kCH - 1)) * 8, kbuf(SLOT) + row0 * D);
-        lds_copy16(gv + ((pc ^ (2 * (row & 3))) & (kCH - 1)) * 8, vbuf(SLOT) + row0 * D);
+        lds_copy16(gv + v_chunk_at<D>(pc, row) * 8, vbuf(SLOT) + row0 * D);
     };
     //  Full tiles: a buffer resource whose base is the tile's row 0 plus a
     //  32-bit per-lane offset (row * token stride + chunk), fixed per tensor.
@@ -434,7 +452,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         kch[i] = (uint32_t)((lane_pc ^ swz_k(r_lane[i])) & (kCH - 1)) << 4;
     }
     // V chunk: op rows start at multiples of 4, so row & 3 == lane_row & 3
-    const uint32_t vch = (uint32_t)((lane_pc ^ (2 * (lane_row & 3))) & (kCH - 1)) << 4;
+    const uint32_t vch = (uint32_t)v_chunk_at<D>(lane_pc, lane_row) << 4;
 
     u32x4_t rsk = {0u, 0u, 0u, 0x00020000u};   // K and V resources of the current full tile
     u32x4_t rsv = rsk;
@@ -519,7 +537,8 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     int v_lane[kDB];
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
-        v_lane[db] = (8 * h + tr_k) * D + (((8 * db + 4 * tr_half + tr_q) ^ (4 * tr_k)) & (D / 4 - 1)) * 4;
+        v_lane[db] = (8 * h + tr_k) * D +
+                     (2 * v_pos<D>(4 * db + 2 * tr_half + (tr_q >> 1), 8 * h + tr_k) + (tr_q & 1)) * 4;
 
     auto read_k = [&](auto SLOT, auto KB, int ds) __attribute__((always_inline)) {
         constexpr int off = decltype(KB)::value * 32 * D;
