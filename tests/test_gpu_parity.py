@@ -229,6 +229,55 @@ def test_empty_batch_and_empty_rows():
     assert out.shape[0] == 0 and lse.shape == (2, 0)
 
 
+def _aligned_inputs(w, key_gain, seed):
+    """Queries near one direction u; real suffix key j = noise + key_gain(j) * u,
+    so score size follows key_gain along the suffix (prefix keys and all
+    values N(0, 1))."""
+    x = synth.make_inputs(w)
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(w.d)
+    u /= np.linalg.norm(u)
+    q = 0.3 * rng.standard_normal((x["q"].shape[0], w.hq, w.d)) + 4.0 * u
+    x["q"] = synth.round_to_bf16_bits(q.astype(np.float32))
+    k = 0.3 * rng.standard_normal((x["k_suffix"].shape[0], w.hkv, w.d))
+    g = key_gain(np.arange(x["k_suffix"].shape[0]))
+    k += g[:, None, None] * u
+    x["k_suffix"] = synth.round_to_bf16_bits(k.astype(np.float32))
+    return x
+
+
+def test_reference_moves_with_growing_scores():
+    """Scores grow along the suffix by ~7.5 (log2 units) per 32-key unit, to
+    ~210 above the prefix keys: the running reference of the lazy softmax has
+    to move at every unit (weights against the first reference would
+    overflow fp32), rescaling O and the row sums each time.  The real suffix
+    is a whole number of 64-key tiles, so the mixed first tile holds prefix
+    keys only and the walk meets the suffix in ascending order."""
+    w = synth.custom_workload(4, 2, 128, [40], [896], [12], "suffix", wid=680)
+    x = _aligned_inputs(w, lambda j: 0.5 * j, seed=681)
+    o, l = gh.run(x)
+    gh.assert_parity_full(w, x, *gh.host(o, l))
+    # cut into key ranges: the pieces' log-sum-exps differ by tens of units
+    dev = gh.device_inputs(x)
+    o, l = jpa.jpa_forward_ws(dev["q"], dev["k_prefix"], dev["v_prefix"], dev["k_suffix"], dev["v_suffix"],
+                              x["cu_q"], x["cu_prefix"], x["cu_suffix_real"], x["scale"], split_wgs=5)
+    torch.cuda.synchronize()
+    gh.assert_parity_full(w, x, *gh.host(o, l))
+
+
+def test_late_spike_key():
+    """One key in the middle of the suffix scores ~78 (log2 units) above all
+    others: the reference jumps once, everything accumulated before it
+    underflows, and each output is that key's value row."""
+    w = synth.custom_workload(4, 4, 128, [64], [640], [0], "suffix", wid=690)
+    x = _aligned_inputs(w, lambda j: np.where(j == 333, 180.0, 0.0), seed=691)
+    o, l = gh.run(x)
+    gh.assert_parity_full(w, x, *gh.host(o, l))
+    vs = synth.bf16_bits_to_f32(x["v_suffix"])
+    got = gh.host(o, l)[0]
+    assert np.max(np.abs(got - vs[333][None])) < 1e-2
+
+
 def _random_case(seed):
     """A seeded random layout: 1-5 rows, prefix / real suffix / pad lengths
     from empty to a few tiles (ragged), GQA group 1-4, D 64 or 128, queries
