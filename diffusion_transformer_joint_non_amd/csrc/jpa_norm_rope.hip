@@ -126,7 +126,9 @@ __global__ __launch_bounds__(kThreads) void jpa_norm_rope_kernel(const jpa_norm_
                 const uint16_t* const xb = k_row ? p.x[1] : p.x[0];
                 const uint32_t xts = (uint32_t)(k_row ? p.x_ts[1] : p.x_ts[0]);
                 const uint32_t xhs = (uint32_t)(k_row ? p.x_hs[1] : p.x_hs[0]);
-                xv[u] = *reinterpret_cast<const u32x4_t*>(xb + (uint64_t)t32 * xts + ((uint32_t)hh[u] * xhs + (uint32_t)e0));
+                // q/k rows are read once: a streaming (non-temporal) load
+                xv[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t*>(xb + (uint64_t)t32 * xts + ((uint32_t)hh[u] * xhs + (uint32_t)e0)));
             }
             if constexpr (VEC) {
                 if (act[u] && rotated) {
@@ -227,7 +229,11 @@ __global__ __launch_bounds__(kThreads) void jpa_norm_rope_kernel(const jpa_norm_
                 uint16_t* const yb = s ? p.y[1] : p.y[0];
                 const uint32_t yts = (uint32_t)(s ? p.y_ts[1] : p.y_ts[0]);
                 const uint32_t yhs = (uint32_t)(s ? p.y_hs[1] : p.y_hs[0]);
-                *reinterpret_cast<u32x4_t*>(yb + (uint64_t)(uint32_t)tt[u] * yts + ((uint32_t)hh[u] * yhs + (uint32_t)e0)) = o;
+                // written once: a streaming store (5% faster back to back than
+                // cached loads and stores of q/k; the table stays cached, every
+                // head of a token reads its row)
+                __builtin_nontemporal_store(
+                    o, reinterpret_cast<u32x4_t*>(yb + (uint64_t)(uint32_t)tt[u] * yts + ((uint32_t)hh[u] * yhs + (uint32_t)e0)));
             }
         }
     }
