@@ -8,7 +8,9 @@ attention forward (libjpa, gfx950) on one MI355X.
     python bench.py --op cat_pad
 
 One step = one jpa_forward_ws call over the whole workload (all query rows of
-all heads, inputs already resident in HBM).  Prints ONE JSON line:
+all heads, inputs already resident in HBM).  Without --warmup / --steps the
+run warms up for at least 0.25 s of back-to-back GPU work, past the clock's
+power-management transient, and times at least 0.1 s.  Prints ONE JSON line:
 
 * value / ms_per_step: valid-token TFLOP/s of the timed steps
   (FLOPs = sum_b Hq * 4 * D * Nq_b * Nk_b, from jpa_plan);
@@ -115,6 +117,38 @@ def timed_steps(step, steps: int, stream):
     return wall_ms, region_ms, per
 
 
+# Default warmup and timed lengths, in seconds of back-to-back GPU work.  On
+# MI355X the first ~0.1 s of continuous load runs up to 25% slower while
+# power management settles (a trace of 2000 back-to-back attention launches
+# repeats to within ~1% from launch ~400 on); timing inside that transient
+# would report the settling, not the sustained rate.
+WARMUP_SECONDS = 0.25
+TIMED_SECONDS = 0.1
+
+
+def resolve_counts(args, step, stream):
+    """--warmup / --steps as given; each one left out is derived from the
+    duration of one step: warm up for at least WARMUP_SECONDS (and 20 steps),
+    time at least TIMED_SECONDS (and 30 steps).  Sets args.warmup/args.steps
+    (the JSON line reports them)."""
+    if args.warmup is not None and args.steps is not None:
+        return
+    import torch
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = max(e0.elapsed_time(e1) * 1e-3, 1e-6)
+    if args.warmup is None:
+        args.warmup = max(20, int(np.ceil(WARMUP_SECONDS / t)))
+    if args.steps is None:
+        args.steps = max(30, int(np.ceil(TIMED_SECONDS / t)))
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -201,6 +235,7 @@ def bench_norm_rope(args):
         jpa.jpa_qk_norm_rope(q, k, wq, wk, table, w.rotary_dim, w.interleaved, w.eps,
                              q_out=qo, k_out=ko, stream=stream)
 
+    resolve_counts(args, step, stream)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -275,6 +310,7 @@ def bench_cat_pad(args):
         for c, _, x, cache, out in data:
             jpa.jpa_causal_cat_pad(x, cache, c.padding, out=out, stream=stream)
 
+    resolve_counts(args, step, stream)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -317,8 +353,10 @@ def bench_cat_pad(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: at least 0.1 s of GPU work, at least 30)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: at least 0.25 s of GPU work, at least 20)")
     ap.add_argument("--workload", type=int, default=None)
     ap.add_argument("--op", choices=("attention", "norm_rope", "rank_share", "cat_pad"), default="attention")
     ap.add_argument("--sp", type=int, default=8, help="rank_share: ranks of the head split")
@@ -337,7 +375,7 @@ def main():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(1)
     if args.copy_probe:
-        copy_probe(args.copy_probe, max(args.steps, 1))
+        copy_probe(args.copy_probe, max(args.steps or 3, 1))
         return
 
     if args.op == "norm_rope":
@@ -388,6 +426,7 @@ def main():
                            dev["v_suffix"], x["cu_q"], x["cu_prefix"], x["cu_suffix_real"],
                            x["scale"], out=out, lse=lse, stream=stream, workspace="auto")
 
+    resolve_counts(args, step, stream)
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
