@@ -848,18 +848,28 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     }   // pieces
 }
 
-// Merge of the cut items: one workgroup per item of the split part of the
-// launch (items n_dp ..), its waves and lanes holding the same rows and
-// features as in jpa_fwd_kernel.  The pieces of an item are those of ranges
-// w_first .. w_last (a piece is slot 2w when it is the first piece of range
-// w, else 2w + 1); they are combined in range order with the log-sum-exp
-// merge of softmax partials:
-//   lse = log2 sum_k 2^lse_k,  out = sum_k 2^(lse_k - lse) * O_k.
-// Items that no range cut were written by jpa_fwd_kernel and are skipped.
+// Merge of the cut items: one workgroup per (item of the split part of the
+// launch, items n_dp .., 64-row block of that item = one wave of
+// jpa_fwd_kernel); its D/32 waves take one 32-feature block each, lanes
+// holding the same rows and features as in jpa_fwd_kernel.  The pieces of an
+// item are those of ranges w_first .. w_last (a piece is slot 2w when it is
+// the first piece of range w, else 2w + 1; only range w_first's piece can be
+// a second one); they are combined with the log-sum-exp merge of softmax
+// partials:
+//   lse = log2 sum_k 2^lse_k,  out = sum_k 2^(lse_k - lse) * O_k,
+// kPieceBatch pieces at a time, so that their loads are in flight together
+// (a wave walking the pieces one by one waited two memory round trips per
+// piece).  Items that no range cut were written by jpa_fwd_kernel and are
+// skipped.
+constexpr int kPieceBatch = 4;
+
 template <int D>
-__global__ __launch_bounds__(kBM, 1)
+__global__ __launch_bounds__(2 * D)
 void jpa_merge_kernel(const jpa_kernel_params p) {
-    const int item = p.n_dp + blockIdx.x;
+    constexpr int kDB = D / 32;
+    constexpr int kCH = D / 8;
+    const int item = p.n_dp + (int)(blockIdx.x / kWaves);
+    const int rblk = (int)(blockIdx.x % kWaves);           // 64-row block of the item
     const int hq = item / p.total_tiles;
     const int tile = item - hq * p.total_tiles;
     int b = 0;
@@ -885,58 +895,111 @@ void jpa_merge_kernel(const jpa_kernel_params p) {
     const int w_first = (int)(((A + 1) * skn - 1) / p.tail_units);
     const int w_last = (int)(((A + ntiles) * skn - 1) / p.tail_units);
     if (w_first == w_last) return;                   // whole item: written directly
-    auto slot_of = [&](int w) { return A <= w * p.tail_units / skn ? 2 * w : 2 * w + 1; };
+    const int s_first = A <= (int64_t)w_first * p.tail_units / skn ? 2 * w_first : 2 * w_first + 1;
+    auto slot_of = [&](int w) { return w == w_first ? s_first : 2 * w; };
 
-    constexpr int kDB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t lds_o[kWaves * 64 * D];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_o[64 * D];
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int j = lane & 31;
-    const int r0 = m0 + wave * (kQB * 32);                 // first row of this wave
+    const int db = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // 32-feature block
+    const int j = lane & 31, h = lane >> 5;
+    const int rowb = rblk * (kQB * 32);                    // first row of the block within the item
+    const int r0 = m0 + rowb;
+
+    // LSE of each row over all pieces, accumulated online
+    float mx[kQB], sm[kQB];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) { mx[qb] = -INFINITY; sm[qb] = 0.f; }
+    for (int w0 = w_first; w0 <= w_last; w0 += kPieceBatch) {
+        float l[kPieceBatch][kQB];
+#pragma unroll
+        for (int k = 0; k < kPieceBatch; ++k)
+            if (w0 + k <= w_last) {
+                const size_t base = (size_t)slot_of(w0 + k) * kBM + rowb + j;
+#pragma unroll
+                for (int qb = 0; qb < kQB; ++qb) l[k][qb] = p.ws_lse[base + qb * 32];
+            }
+#pragma unroll
+        for (int k = 0; k < kPieceBatch; ++k)
+            if (w0 + k <= w_last) {
+#pragma unroll
+                for (int qb = 0; qb < kQB; ++qb) {
+                    const float mn = fmaxf(mx[qb], l[k][qb]);
+                    sm[qb] = sm[qb] * __builtin_amdgcn_exp2f(mx[qb] - mn) + __builtin_amdgcn_exp2f(l[k][qb] - mn);
+                    mx[qb] = mn;
+                }
+            }
+    }
     float lse2[kQB];
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-        const int row = wave * (kQB * 32) + qb * 32 + j;
-        float mx = -INFINITY;
-        for (int w = w_first; w <= w_last; ++w) mx = fmaxf(mx, p.ws_lse[(size_t)slot_of(w) * kBM + row]);
-        float sum = 0.f;
-        for (int w = w_first; w <= w_last; ++w)
-            sum += __builtin_amdgcn_exp2f(p.ws_lse[(size_t)slot_of(w) * kBM + row] - mx);
-        lse2[qb] = mx + __builtin_amdgcn_logf(sum);
-    }
-    f32x16_t o[kQB][kDB];
+    for (int qb = 0; qb < kQB; ++qb) lse2[qb] = mx[qb] + __builtin_amdgcn_logf(sm[qb]);
+
+    // weighted sum of the pieces' O for this wave's 32 features
+    f32x16_t o[kQB];
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
+    for (int qb = 0; qb < kQB; ++qb) o[qb] = f32x16_t{};
+    for (int w0 = w_first; w0 <= w_last; w0 += kPieceBatch) {
+        float4 x[kPieceBatch][kQB][4];
+        float a[kPieceBatch][kQB];
 #pragma unroll
-        for (int db = 0; db < kDB; ++db) o[qb][db] = f32x16_t{};
-    for (int w = w_first; w <= w_last; ++w) {
-        const int sw = slot_of(w);
-        const float* const so = p.ws_o + (size_t)sw * kBM * D + (size_t)wave * (kQB * 32) * D;
+        for (int k = 0; k < kPieceBatch; ++k)
+            if (w0 + k <= w_last) {
+                const int sw = slot_of(w0 + k);
+                const float* const so = p.ws_o + (size_t)sw * kBM * D + (size_t)rowb * D;
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-            const float a = __builtin_amdgcn_exp2f(
-                p.ws_lse[(size_t)sw * kBM + wave * (kQB * 32) + qb * 32 + j] - lse2[qb]);
+                for (int qb = 0; qb < kQB; ++qb) {
+                    a[k][qb] = p.ws_lse[(size_t)sw * kBM + rowb + qb * 32 + j];
 #pragma unroll
-            for (int db = 0; db < kDB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float4 x =
-                        *reinterpret_cast<const float4*>(so + ((size_t)((qb * kDB + db) * 4 + g) * 64 + lane) * 4);
-                    o[qb][db][4 * g] += a * x.x;
-                    o[qb][db][4 * g + 1] += a * x.y;
-                    o[qb][db][4 * g + 2] += a * x.z;
-                    o[qb][db][4 * g + 3] += a * x.w;
+                    for (int g = 0; g < 4; ++g)
+                        x[k][qb][g] = *reinterpret_cast<const float4*>(
+                            so + ((size_t)((qb * kDB + db) * 4 + g) * 64 + lane) * 4);
                 }
+            }
+#pragma unroll
+        for (int k = 0; k < kPieceBatch; ++k)
+            if (w0 + k <= w_last) {
+#pragma unroll
+                for (int qb = 0; qb < kQB; ++qb) {
+                    const float wt = __builtin_amdgcn_exp2f(a[k][qb] - lse2[qb]);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        o[qb][4 * g] += wt * x[k][qb][g].x;
+                        o[qb][4 * g + 1] += wt * x[k][qb][g].y;
+                        o[qb][4 * g + 2] += wt * x[k][qb][g].z;
+                        o[qb][4 * g + 3] += wt * x[k][qb][g].w;
+                    }
+                }
+            }
+    }
+
+    // bf16 rows through LDS (16-byte chunks XOR-swizzled by row, as in
+    // store_rows_bf16), then whole 16-byte row chunks to out
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+        const int row = 32 * qb + j;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int c = 4 * db + g;
+            const u32x2_t v = {pack_bf16(o[qb][4 * g], o[qb][4 * g + 1]), pack_bf16(o[qb][4 * g + 2], o[qb][4 * g + 3])};
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
+                (lds_u16*)lds_o + row * D + ((c ^ (row & (kCH - 1))) * 8) + 4 * h) = v;
         }
     }
-    float one[kQB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) one[qb] = 1.f;
+    __syncthreads();
     const int q_start = p.rows[b].q_start, q_real = p.rows[b].q_real, q_slots = p.rows[b].q_slots;
-    store_rows_bf16<D>(o, one, (lds_u16*)(lds_o + wave * 64 * D),
-                       p.out + (int64_t)hq * p.o_hs + (int64_t)(q_start + r0) * p.o_ts, p.o_ts,
-                       q_real - r0, q_slots - r0, lane);
-    if (p.lse && lane < 32) {
+    uint16_t* const out_row0 = p.out + (int64_t)hq * p.o_hs + (int64_t)(q_start + r0) * p.o_ts;
+    constexpr int kThreadsM = 64 * kDB;
+#pragma unroll
+    for (int i = 0; i < 64 * kCH / kThreadsM; ++i) {
+        const int id = i * kThreadsM + (int)threadIdx.x;
+        const int row = id / kCH, c = id % kCH;
+        u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+            (lds_u16*)lds_o + row * D + ((c ^ (row & (kCH - 1))) * 8));
+        if (r0 + row < q_slots) {
+            if (r0 + row >= q_real) v = u32x4_t{0u, 0u, 0u, 0u};        // pad row: +0.0
+            *reinterpret_cast<u32x4_t*>(out_row0 + (int64_t)row * p.o_ts + 8 * c) = v;
+        }
+    }
+    if (p.lse && db == 0 && lane < 32) {
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
             const int qi = r0 + qb * 32 + j;
@@ -963,9 +1026,9 @@ int jpa_launch_kernel(const jpa_kernel_params& p, int head_dim, void* stream) {
     // kernel on the same stream (it sees the partials once the first ends)
     const int tail_items = p.total_tiles * p.hq - p.n_dp;
     if (head_dim == 128)
-        hipLaunchKernelGGL(jpa_merge_kernel<128>, dim3(tail_items), dim3(kBM), 0, s, p);
+        hipLaunchKernelGGL(jpa_merge_kernel<128>, dim3(tail_items * kWaves), dim3(2 * 128), 0, s, p);
     else
-        hipLaunchKernelGGL(jpa_merge_kernel<64>, dim3(tail_items), dim3(kBM), 0, s, p);
+        hipLaunchKernelGGL(jpa_merge_kernel<64>, dim3(tail_items * kWaves), dim3(2 * 64), 0, s, p);
     return (int)hipGetLastError();
 }
 
