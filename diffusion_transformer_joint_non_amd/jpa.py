@@ -88,6 +88,11 @@ def load_library() -> ctypes.CDLL:
         raise RuntimeError(
             f"libjpa.so not found at {_LIB_PATH}; build it with "
             "`python -m diffusion_transformer_joint_non_amd.build`")
+    # Bind to the HIP runtime PyTorch uses: torch ships its own libamdhip64,
+    # and the library's dependency on that soname resolves to whichever copy
+    # is loaded first.  Loaded before torch, the library would bring in a
+    # second runtime, and its calls would not see torch's device state.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(_LIB_PATH)
     tp = ctypes.POINTER(JpaTensor)
     i32p = ctypes.POINTER(ctypes.c_int32)

@@ -316,3 +316,27 @@ def test_parity_random_layouts(seed):
         out, lse = gh.host(o, l)
         gh.assert_parity_full(w, x, out, lse)
         gh.assert_pad_rows(w, out, lse)
+
+
+def test_library_loaded_before_torch_still_runs():
+    """The binding binds libjpa to the HIP runtime PyTorch uses even when
+    load_library() runs before any torch import (torch ships its own
+    libamdhip64; a second runtime in the process made every call fail with a
+    HIP error).  Checked in a fresh interpreter."""
+    import subprocess
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from diffusion_transformer_joint_non_amd import jpa\n"
+        "jpa.load_library()\n"
+        "import numpy as np, torch, synth, oracle\n"
+        "w = synth.WORKLOADS[1]; x = synth.make_inputs(w)\n"
+        "d = [torch.from_numpy(np.ascontiguousarray(x[n]).view(np.int16)).view(torch.bfloat16).cuda()\n"
+        "     for n in ('q', 'k_prefix', 'v_prefix', 'k_suffix', 'v_suffix')]\n"
+        "o, l = jpa.jpa_forward(*d, x['cu_q'], x['cu_prefix'], x['cu_suffix_real'], x['scale'])\n"
+        "torch.cuda.synchronize()\n"
+        "print('ok', bool(torch.isfinite(o.float()).all()))\n" % root)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "ok True" in r.stdout
