@@ -22,7 +22,9 @@ power-management transient, and times at least 0.1 s.  Prints ONE JSON line:
 * parity: the GPU result of the timed call against that oracle run.
 
 Options for profiling runs: --no-cpu-baseline, --copy-probe BYTES (time a plain
-device copy of that many bytes; used to calibrate rocprofv3 HBM counters).
+device copy of that many bytes; used to calibrate rocprofv3 HBM counters),
+--split-wgs N (force the balanced last round over N key ranges; a step is then
+the main kernel plus the merge kernel, and no traffic figure is reported).
 
 --op norm_rope measures the step before attention instead: per-head Q/K
 RMSNorm + rotary embedding (jpa_qk_norm_rope) on the q/k shapes of a norm-rope
@@ -363,6 +365,9 @@ def main():
     ap.add_argument("--rank", type=int, default=0, help="rank_share: which rank's share")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
+    ap.add_argument("--split-wgs", type=int, default=0,
+                    help="attention: force the balanced last round over this many key ranges "
+                         "(0: the library decides)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -424,7 +429,8 @@ def main():
     def step():
         jpa.jpa_forward_ws(dev["q"], dev["k_prefix"], dev["v_prefix"], dev["k_suffix"],
                            dev["v_suffix"], x["cu_q"], x["cu_prefix"], x["cu_suffix_real"],
-                           x["scale"], out=out, lse=lse, stream=stream, workspace="auto")
+                           x["scale"], out=out, lse=lse, stream=stream, workspace="auto",
+                           split_wgs=args.split_wgs)
 
     resolve_counts(args, step, stream)
     log(f"warmup {args.warmup}")
@@ -437,7 +443,8 @@ def main():
     log(f"timing {args.steps} steps")
     ms_per_step, kern_ms, per_launch_ms = timed_steps(step, args.steps, stream)
     achieved = flops / (kern_ms * 1e-3) / 1e12
-    traffic = load_traffic(w.name)
+    # the committed counters cover the library's own choice of path
+    traffic = load_traffic(w.name) if args.split_wgs == 0 else None
     # Launch-bound sizes: the per-call time when the host is out of the way,
     # from a HIP graph of 20 calls replayed (the library allocates nothing and
     # never synchronises, so its calls capture as they are).
@@ -452,17 +459,25 @@ def main():
                     jpa.jpa_forward_ws(dev["q"], dev["k_prefix"], dev["v_prefix"], dev["k_suffix"],
                                        dev["v_suffix"], x["cu_q"], x["cu_prefix"], x["cu_suffix_real"],
                                        x["scale"], out=out, lse=lse, stream=cs,
-                                       workspace=jpa.workspace_for(out.device, stream.cuda_stream, w.d))
+                                       workspace=jpa.workspace_for(out.device, stream.cuda_stream, w.d,
+                                                                   args.split_wgs),
+                                       split_wgs=args.split_wgs)
         torch.cuda.synchronize()
-        g.replay()
+        # the same time-based warmup and timed length as the eager steps: the
+        # pause for capture lets the clocks settle back to their idle state
+        per_replay_s = 20 * kern_ms * 1e-3
+        n_warm = max(5, int(np.ceil(WARMUP_SECONDS / per_replay_s)))
+        n_timed = max(5, int(np.ceil(TIMED_SECONDS / per_replay_s)))
+        for _ in range(n_warm):
+            g.replay()
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record()
-        for _ in range(5):
+        for _ in range(n_timed):
             g.replay()
         g1.record()
         torch.cuda.synchronize()
-        graph_us = g0.elapsed_time(g1) * 1e3 / (5 * 20)
+        graph_us = g0.elapsed_time(g1) * 1e3 / (n_timed * 20)
     # minimum bytes a call moves: real q read, every out slot written, each
     # row's real prefix/suffix K and V read once, lse written
     real_q = int(sum(r[2] for r in rows))
@@ -487,7 +502,8 @@ def main():
                    "head_dim": w.d, "prefix": list(map(int, w.prefix)),
                    "suffix_real": list(map(int, w.suffix_real)),
                    "suffix_pad": list(map(int, w.suffix_pad)), "queries": w.queries,
-                   "valid_flops": flops, **({"rank_share": share} if share else {})},
+                   "valid_flops": flops, **({"rank_share": share} if share else {}),
+                   **({"split_wgs": args.split_wgs} if args.split_wgs else {})},
         "pct_of_bf16_peak": round(100.0 * flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
