@@ -36,6 +36,17 @@ def run(x, dev=None, scale=None, with_lse=True, out=None, lse=None, **override):
     return o, l
 
 
+def run_ws(x, dev=None):
+    """The call bench.py times: jpa_forward_ws with its cached workspace, the
+    library deciding whether to balance the last round of work items."""
+    dev = dev or device_inputs(x)
+    o, l = jpa.jpa_forward_ws(dev["q"], dev["k_prefix"], dev["v_prefix"], dev["k_suffix"],
+                              dev["v_suffix"], x["cu_q"], x["cu_prefix"], x["cu_suffix_real"],
+                              x["scale"], workspace="auto")
+    torch.cuda.synchronize()
+    return o, l
+
+
 def host(o, l):
     """bf16 out -> float32 numpy, lse -> float32 numpy."""
     return o.float().cpu().numpy(), (None if l is None else l.cpu().numpy())
@@ -53,9 +64,13 @@ def assert_pad_rows(w, out, lse):
         assert np.all(lse[:, pad] == -np.inf), "pad query rows must get LSE = -inf"
 
 
-def assert_parity_full(w, x, out, lse, scale=None):
-    ref_o, ref_l = oracle.attention(*[x[n] for n in NAMES], x["cu_q"], x["cu_prefix"],
-                                    x["cu_suffix_real"], x["scale"] if scale is None else scale)
+def oracle_full(x, scale=None):
+    return oracle.attention(*[x[n] for n in NAMES], x["cu_q"], x["cu_prefix"],
+                            x["cu_suffix_real"], x["scale"] if scale is None else scale)
+
+
+def assert_parity_full(w, x, out, lse, scale=None, ref=None):
+    ref_o, ref_l = oracle_full(x, scale) if ref is None else ref
     real = ~w.pad_query_mask()
     err = oracle.compare(out[real], lse[:, real].T if lse is not None else np.zeros(0),
                          ref_o[real], ref_l[:, real].T if lse is not None else np.zeros(0))

@@ -61,14 +61,23 @@ def test_parity_small_cases(ci):
 
 @pytest.mark.parametrize("wid", [1, 2, 3])
 def test_parity_workload_full(wid):
+    """Every output of jpa_forward and of the call bench.py times
+    (jpa_forward_ws, which balances the last round on the CFG pair) against
+    the oracle."""
     w = synth.WORKLOADS[wid]
     _say(f"workload {wid} ({w.name}): generating inputs")
     x = synth.make_inputs(w)
-    o, l = gh.run(x)
-    out, lse = gh.host(o, l)
+    dev = gh.device_inputs(x)
+    res = {}
+    for name, call in (("jpa_forward", gh.run), ("bench path", gh.run_ws)):
+        o, l = call(x, dev)
+        res[name] = gh.host(o, l)
+        del o, l
     _say(f"workload {wid}: GPU done, running oracle")
-    err = gh.assert_parity_full(w, x, out, lse)
-    _say(f"workload {wid}: {err}")
+    ref = gh.oracle_full(x)
+    for name, (out, lse) in res.items():
+        err = gh.assert_parity_full(w, x, out, lse, ref=ref)
+        _say(f"workload {wid} {name}: {err}")
     rows, flops = jpa.jpa_plan(x["cu_q"], x["cu_prefix"], x["cu_suffix_real"], w.hq, w.d)
     assert flops == oracle.valid_flops(oracle.decode_segments(
         x["cu_q"], x["cu_prefix"], x["cu_suffix_real"]), w.hq, w.d)
@@ -76,21 +85,29 @@ def test_parity_workload_full(wid):
 
 @pytest.mark.parametrize("wid", [4, 5])
 def test_parity_workload_sampled(wid):
+    """Sampled rows of jpa_forward and of the call bench.py times
+    (jpa_forward_ws, which balances the last round on the long GQA workload)
+    against the oracle; pad rows in full."""
     from oracle_pool import oracle_rows_parallel
     w = synth.WORKLOADS[wid]
     _say(f"workload {wid} ({w.name}): generating inputs")
     x = synth.make_inputs(w)
-    o, l = gh.run(x)
-    out, lse = gh.host(o, l)
-    del o, l
+    dev = gh.device_inputs(x)
+    res = {}
+    for name, call in (("jpa_forward", gh.run), ("bench path", gh.run_ws)):
+        o, l = call(x, dev)
+        res[name] = gh.host(o, l)
+        del o, l
+    del dev
     torch.cuda.empty_cache()
     rows = synth.sample_query_rows(w, 4096)
     _say(f"workload {wid}: GPU done, oracle on {rows.shape[1]} rows x {w.hq} heads")
     ref_o, ref_l = oracle_rows_parallel(x, rows)
-    err = gh.assert_parity_rows(out, lse, rows, ref_o, ref_l)
-    gh.assert_pad_rows(w, out, lse)
-    assert np.isfinite(out).all() and np.isfinite(lse[:, ~w.pad_query_mask()]).all()
-    _say(f"workload {wid}: {err}")
+    for name, (out, lse) in res.items():
+        err = gh.assert_parity_rows(out, lse, rows, ref_o, ref_l)
+        gh.assert_pad_rows(w, out, lse)
+        assert np.isfinite(out).all() and np.isfinite(lse[:, ~w.pad_query_mask()]).all()
+        _say(f"workload {wid} {name}: {err}")
 
 
 @pytest.mark.parametrize("case", [(1, None), (None, 1)])
