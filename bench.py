@@ -24,7 +24,8 @@ power-management transient, and times at least 0.1 s.  Prints ONE JSON line:
 Options for profiling runs: --no-cpu-baseline, --copy-probe BYTES (time a plain
 device copy of that many bytes; used to calibrate rocprofv3 HBM counters),
 --split-wgs N (force the balanced last round over N key ranges; a step is then
-the main kernel plus the merge kernel, and no traffic figure is reported).
+the main kernel plus the merge kernel; -1 never splits), with no traffic
+figure reported for either.
 
 --op norm_rope measures the step before attention instead: per-head Q/K
 RMSNorm + rotary embedding (jpa_qk_norm_rope) on the q/k shapes of a norm-rope
@@ -367,7 +368,7 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0)
     ap.add_argument("--split-wgs", type=int, default=0,
                     help="attention: force the balanced last round over this many key ranges "
-                         "(0: the library decides)")
+                         "(0: the library decides; -1: no workspace, jpa_forward's path)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -429,8 +430,9 @@ def main():
     def step():
         jpa.jpa_forward_ws(dev["q"], dev["k_prefix"], dev["v_prefix"], dev["k_suffix"],
                            dev["v_suffix"], x["cu_q"], x["cu_prefix"], x["cu_suffix_real"],
-                           x["scale"], out=out, lse=lse, stream=stream, workspace="auto",
-                           split_wgs=args.split_wgs)
+                           x["scale"], out=out, lse=lse, stream=stream,
+                           workspace=None if args.split_wgs < 0 else "auto",
+                           split_wgs=max(args.split_wgs, 0))
 
     resolve_counts(args, step, stream)
     log(f"warmup {args.warmup}")
@@ -459,9 +461,9 @@ def main():
                     jpa.jpa_forward_ws(dev["q"], dev["k_prefix"], dev["v_prefix"], dev["k_suffix"],
                                        dev["v_suffix"], x["cu_q"], x["cu_prefix"], x["cu_suffix_real"],
                                        x["scale"], out=out, lse=lse, stream=cs,
-                                       workspace=jpa.workspace_for(out.device, stream.cuda_stream, w.d,
-                                                                   args.split_wgs),
-                                       split_wgs=args.split_wgs)
+                                       workspace=None if args.split_wgs < 0 else jpa.workspace_for(
+                                           out.device, stream.cuda_stream, w.d, args.split_wgs),
+                                       split_wgs=max(args.split_wgs, 0))
         torch.cuda.synchronize()
         # the same time-based warmup and timed length as the eager steps: the
         # pause for capture lets the clocks settle back to their idle state
