@@ -315,14 +315,18 @@ def _random_case(seed):
     return synth.custom_workload(hq, hkv, d, prefix, real, pad, queries, wid=500 + seed)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(32))
 def test_parity_random_layouts(seed):
     w = _random_case(seed)
     x = synth.make_inputs(w, pad_fill="garbage")
     _say(f"random layout {seed}: hq={w.hq} hkv={w.hkv} d={w.d} P={w.prefix} R={w.suffix_real} "
          f"pad={w.suffix_pad} q={w.queries}")
-    for split in (None, 16):
-        dev = gh.device_inputs(x)
+    # jpa_forward; forced splits over 16 and over a seeded 1-299 key ranges
+    # (pieces then start and end anywhere in the key walk); the automatic choice
+    n_ranges = int(np.random.default_rng(9000 + seed).integers(1, 300))
+    dev = gh.device_inputs(x)
+    ref = gh.oracle_full(x)
+    for split in (None, 16, n_ranges, 0):
         if split is None:
             o, l = gh.run(x, dev)
         else:
@@ -331,7 +335,7 @@ def test_parity_random_layouts(seed):
                                       x["scale"], split_wgs=split)
             torch.cuda.synchronize()
         out, lse = gh.host(o, l)
-        gh.assert_parity_full(w, x, out, lse)
+        gh.assert_parity_full(w, x, out, lse, ref=ref)
         gh.assert_pad_rows(w, out, lse)
 
 
