@@ -98,6 +98,26 @@ def test_parity_small(case):
     _assert_close(ko, rk)
 
 
+def _random_case(seed):
+    """A seeded random call: 1-400 tokens, 1-8 q heads and 1-8 k heads, head_dim
+    64/128/256, any even rotary_dim from 0 (plain RMSNorm) to head_dim, either
+    pair layout."""
+    rng = np.random.default_rng(7100 + seed)
+    d = int(rng.choice([64, 128, 256]))
+    return (int(rng.integers(1, 401)), int(rng.integers(1, 9)), int(rng.integers(1, 9)), d,
+            2 * int(rng.integers(0, d // 2 + 1)), bool(rng.integers(0, 2)), float(rng.choice([1e-6, 1e-5])))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_parity_random(seed):
+    case = _random_case(seed)
+    w, x = _inputs(*case, seed=40 + seed)
+    qo, ko = _run(x)
+    rq, rk = _oracle(x)
+    _assert_close(qo, rq)
+    _assert_close(ko, rk)
+
+
 @pytest.mark.parametrize("wid", [1, 2, 3])
 def test_parity_workloads_full(wid):
     w = synth.NORM_ROPE_WORKLOADS[wid]
