@@ -3,13 +3,17 @@
     python -m diffusion_transformer_joint_non_amd.build
 
 The library lands in ``diffusion_transformer_joint_non_amd/_lib/libjpa.so``;
-the Python binding loads it from there and nowhere else.
+the Python binding loads it from there and nowhere else.  A check build of the
+same sources, ``libjpa_strict_waits.so`` (JPA_STRICT_WAITS: the attention
+kernel waits for every tile copy at each barrier), is built beside it for the
+GPU test that compares the two bit for bit.
 """
 
 import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -17,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIB_DIR, "libjpa.so")
+STRICT_LIB = os.path.join(LIB_DIR, "libjpa_strict_waits.so")
 ARCH = "gfx950"
 
 SOURCES = ["jpa_kernel.hip", "jpa_host.cpp", "jpa_norm_rope.hip", "jpa_norm_rope_host.cpp",
@@ -44,9 +49,9 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = True, extra_flags=None) -> str:
+def build(verbose: bool = True, extra_flags=None, lib: str = LIB) -> str:
     os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}",
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
@@ -59,9 +64,17 @@ def build(verbose: bool = True, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build_all(verbose: bool = True) -> list:
+    """The library and its strict-waits check build, compiled side by side."""
+    with ThreadPoolExecutor(2) as ex:
+        jobs = [ex.submit(build, verbose),
+                ex.submit(build, verbose, ["-DJPA_STRICT_WAITS"], STRICT_LIB)]
+        return [j.result() for j in jobs]
 
 
 if __name__ == "__main__":
-    print(build())
+    print("\n".join(build_all()))

@@ -240,7 +240,15 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     // of this wave) stay in flight: s_waitcnt vmcnt(N) lgkmcnt(0); s_barrier.
     // gfx9 s_waitcnt fields: vmcnt[3:0] bits 3:0, expcnt bits 6:4,
     // lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14.
+#ifndef JPA_STRICT_WAITS
     constexpr int kWaitVm = 2 * kOpsPerWave;
+#else
+    // Check build: every copy, the newest prefetch included, lands before each
+    // barrier.  The arithmetic is unchanged, so its results must equal the
+    // release build's bit for bit; a difference would mean a tile was read
+    // before its copy had landed.
+    constexpr int kWaitVm = 0;
+#endif
     constexpr int kWaitImm = (kWaitVm & 15) | (7 << 4) | (0 << 8) | ((kWaitVm >> 4) << 14);
     auto tile_barrier = [&]() __attribute__((always_inline)) {
         asm volatile("" ::: "memory");

@@ -17,6 +17,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libjpa.so")
+STRICT_LIB_PATH = os.path.join(os.path.dirname(_LIB_PATH), "libjpa_strict_waits.so")
 
 JPA_OK = 0
 JPA_ERR_NULL = 1
@@ -84,16 +85,28 @@ def load_library() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    _lib = _open(_LIB_PATH)
+    return _lib
+
+
+def load_strict_waits_library() -> ctypes.CDLL:
+    """The check build of the same sources (JPA_STRICT_WAITS: the attention
+    kernel waits for every tile copy at each barrier), for tests that compare
+    it bit for bit with libjpa.so.  Nothing in this module calls it."""
+    return _open(STRICT_LIB_PATH)
+
+
+def _open(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"libjpa.so not found at {_LIB_PATH}; build it with "
+            f"{os.path.basename(path)} not found at {path}; build it with "
             "`python -m diffusion_transformer_joint_non_amd.build`")
     # Bind to the HIP runtime PyTorch uses: torch ships its own libamdhip64,
     # and the library's dependency on that soname resolves to whichever copy
     # is loaded first.  Loaded before torch, the library would bring in a
     # second runtime, and its calls would not see torch's device state.
     import torch  # noqa: F401
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     tp = ctypes.POINTER(JpaTensor)
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.jpa_forward.restype = ctypes.c_int
@@ -129,7 +142,6 @@ def load_library() -> ctypes.CDLL:
     lib.jpa_qk_norm_rope.restype = ctypes.c_int
     lib.jpa_qk_norm_rope.argtypes = [tp, tp, vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_float, tp, tp, vp]
-    _lib = lib
     return lib
 
 

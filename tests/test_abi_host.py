@@ -1,6 +1,7 @@
 """Host-side checks of the C ABI (no GPU needed; no kernel is run).
 
-* the in-tree libjpa.so loads and exports every function include/*.h declares;
+* the in-tree libjpa.so loads and exports every function include/*.h declares,
+  and so does its strict-waits check build;
 * jpa_plan's integers equal the hand-derived workload bookkeeping and the
   oracle's decoding, bit for bit;
 * every validation error of jpa_validate is reachable from the host;
@@ -40,6 +41,15 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(jpa.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_strict_waits_build_exports_the_same_symbols():
+    """The check build (attention kernel waiting for every tile copy at each
+    barrier) is a drop-in twin of libjpa.so."""
+    lib = jpa.load_strict_waits_library()
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    assert lib.jpa_abi_version() == jpa.load_library().jpa_abi_version()
 
 
 def test_abi_version_and_status_strings():
