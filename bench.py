@@ -2,15 +2,18 @@
 """Throughput of the split prefix/suffix, tail-pad-skipping, non-causal
 attention forward (libjpa, gfx950) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--steps K] [--warmup W] [--workload 5]
     python bench.py --op norm_rope [--workload 4]
     python bench.py --op rank_share [--workload 4] [--sp 8] [--rank 0]
     python bench.py --op cat_pad
 
 One step = one jpa_forward_ws call over the whole workload (all query rows of
-all heads, inputs already resident in HBM).  Without --warmup / --steps the
-run warms up for at least 0.25 s of back-to-back GPU work, past the clock's
-power-management transient, and times at least 0.1 s.  Prints ONE JSON line:
+all heads, inputs already resident in HBM).  The default workload is the
+largest single-GPU one: long video with GQA 40/8, prefix 256, suffix 75600
+real + 176 tail-pad slots.  The run always warms up for at least 0.25 s of
+back-to-back GPU work (past the clock's power-management transient); --warmup
+W only raises the minimum step count.  Without --steps it times at least
+0.1 s.  Prints ONE JSON line:
 
 * value / ms_per_step: valid-token TFLOP/s of the timed steps
   (FLOPs = sum_b Hq * 4 * D * Nq_b * Nk_b, from jpa_plan);
@@ -18,7 +21,10 @@ power-management transient, and times at least 0.1 s.  Prints ONE JSON line:
   launch stream at the two ends of the timed region (nothing is inserted
   between launches), against the bf16 dense MFMA peak; a separate pass with
   an event pair around each launch gives the per-launch spread;
-* cpu_baseline: the fp64 oracle timed on this host's cores;
+* cpu_baseline: the fp64 oracle timed on this host's cores, on the whole
+  workload when it is small, else on the seeded subset of 4096 real query rows
+  per head (every head) that the parity check uses; the full-workload time is
+  extrapolated linearly in valid FLOPs;
 * parity: the GPU result of the timed call against that oracle run.
 
 Options for profiling runs: --no-cpu-baseline, --copy-probe BYTES (time a plain
@@ -56,7 +62,7 @@ PEAK_BF16_TFLOPS = 2500.0        # MI355X published dense bf16 MFMA peak
 KERNEL_NAME = "jpa_fwd_kernel"
 KERNEL_SOURCES = ("diffusion_transformer_joint_non_amd/csrc/jpa_kernel.hip",
                   "diffusion_transformer_joint_non_amd/csrc/jpa_params.h")
-DEFAULT_WORKLOAD = 2
+DEFAULT_WORKLOAD = 5
 
 NR_METRIC = "Q/K RMSNorm+RoPE GB/s (algorithmic HBM bytes) + % of MI355X HBM peak"
 PEAK_HBM_GBS = 8000.0            # MI355X published HBM3E bandwidth
@@ -130,12 +136,11 @@ TIMED_SECONDS = 0.1
 
 
 def resolve_counts(args, step, stream):
-    """--warmup / --steps as given; each one left out is derived from the
-    duration of one step: warm up for at least WARMUP_SECONDS (and 20 steps),
-    time at least TIMED_SECONDS (and 30 steps).  Sets args.warmup/args.steps
-    (the JSON line reports them)."""
-    if args.warmup is not None and args.steps is not None:
-        return
+    """Warmup and timed step counts from the duration of one step.  Warmup
+    always covers at least WARMUP_SECONDS of GPU work; a given --warmup is a
+    minimum step count (default 20).  --steps is used as given, else at least
+    TIMED_SECONDS of GPU work and 30 steps.  Sets args.warmup_run (the warmup
+    steps actually run) and args.steps."""
     import torch
     for _ in range(3):
         step()
@@ -146,55 +151,88 @@ def resolve_counts(args, step, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     t = max(e0.elapsed_time(e1) * 1e-3, 1e-6)
+    floor = int(np.ceil(WARMUP_SECONDS / t))
+    args.warmup_run = max(floor, 20 if args.warmup is None else args.warmup)
     if args.warmup is None:
-        args.warmup = max(20, int(np.ceil(WARMUP_SECONDS / t)))
+        args.warmup = args.warmup_run
     if args.steps is None:
         args.steps = max(30, int(np.ceil(TIMED_SECONDS / t)))
 
 
-def blas_threads() -> int:
+def blas_info():
+    """(threads, library description) of the BLAS NumPy calls into."""
     try:
+        np.dot(np.ones((2, 2)), np.ones((2, 2)))     # make sure the BLAS is loaded
         from threadpoolctl import threadpool_info
-        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
-        if n:
-            return int(max(n))
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            i = max(libs, key=lambda r: r.get("num_threads", 0))
+            desc = f"{i.get('internal_api')} {i.get('version')} ({i.get('architecture')})"
+            return int(i["num_threads"]), desc
     except Exception:
         pass
-    return 1
+    return 1, "unknown"
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_facts():
+    """Where the oracle ran: usable cores, BLAS threads and library, CPU model."""
+    threads, lib = blas_info()
+    return {"cores": len(os.sched_getaffinity(0)), "blas_threads": threads, "blas": lib,
+            "cpu_model": cpu_model()}
+
+
+# Above this much valid work the oracle runs on a seeded random subset of
+# 4096 real query rows per head (every head, every real key) instead of the
+# whole workload: the two largest workloads.
+FULL_ORACLE_MAX_FLOPS = 2.0e12
+SUBSET_ROWS_PER_HEAD = 4096
 
 
 def cpu_baseline(w, x, flops_total):
-    """Time the oracle, as it stands, on the whole workload when that is small
-    enough (about half a minute of CPU work at most), else on a seeded subset of
-    query rows per head; report valid-token TFLOP/s scaled to what was run."""
+    """Time the oracle, as it stands, on the whole workload when that is at
+    most FULL_ORACLE_MAX_FLOPS of valid work, else on the seeded subset of
+    SUBSET_ROWS_PER_HEAD real rows per head (synth.sample_query_rows, every
+    head).
+    value = valid-token TFLOP/s of what was run; the time for the whole
+    workload is extrapolated linearly in valid FLOPs."""
     import oracle
     import synth
     rows_total = int((~w.pad_query_mask()).sum())
-    est_row_s = 4.0e-9 * (w.prefix[0] + w.suffix_real[0]) * (1 + w.d / 64)
-    per_head = rows_total if est_row_s * rows_total * w.hq < 30.0 else max(
-        64, int(20.0 / (est_row_s * w.hq)))
+    names = ("q", "k_prefix", "v_prefix", "k_suffix", "v_suffix", "cu_q", "cu_prefix",
+             "cu_suffix_real")
     t0 = time.perf_counter()
-    if per_head >= rows_total:
-        ref_o, ref_l = oracle.attention(*[x[n] for n in ("q", "k_prefix", "v_prefix", "k_suffix",
-                                                         "v_suffix", "cu_q", "cu_prefix",
-                                                         "cu_suffix_real")], x["scale"])
+    if flops_total <= FULL_ORACLE_MAX_FLOPS or rows_total <= SUBSET_ROWS_PER_HEAD:
+        ref_o, ref_l = oracle.attention(*[x[n] for n in names], x["scale"])
         sample = f"full workload: {rows_total} real query rows x {w.hq} heads"
         flops = flops_total
         rows = None
     else:
-        rows = synth.sample_query_rows(w, per_head)
-        ref_o, ref_l = oracle.attention_rows(*[x[n] for n in (
-            "q", "k_prefix", "v_prefix", "k_suffix", "v_suffix", "cu_q", "cu_prefix",
-            "cu_suffix_real")], x["scale"], rows)
+        rows = synth.sample_query_rows(w, SUBSET_ROWS_PER_HEAD)
+        ref_o, ref_l = oracle.attention_rows(*[x[n] for n in names], x["scale"], rows)
         segs = oracle.decode_segments(x["cu_q"], x["cu_prefix"], x["cu_suffix_real"])
         starts = np.asarray([s.q_start for s in segs])
         keys = np.asarray([s.keys for s in segs])
         owner = np.searchsorted(starts, rows, side="right") - 1
         flops = int(4 * w.d * keys[owner].sum())
-        sample = f"seeded subset: {rows.shape[1]} real query rows per head x {w.hq} heads"
+        sample = (f"seeded subset: {rows.shape[1]} real query rows per head (of {rows_total}) "
+                  f"x all {w.hq} heads, every real key")
     dt = time.perf_counter() - t0
-    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
-            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", **host_facts(),
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 3),
+            "sample_gflops": round(flops / 1e9, 1),
+            "sample_gflop_per_s": round(flops / dt / 1e9, 2),
+            "seconds_full_workload_extrapolated": round(dt * flops_total / flops, 1)}
     return base, ref_o, ref_l, rows
 
 
@@ -239,7 +277,7 @@ def bench_norm_rope(args):
                              q_out=qo, k_out=ko, stream=stream)
 
     resolve_counts(args, step, stream)
-    for _ in range(args.warmup):
+    for _ in range(args.warmup_run):
         step()
     torch.cuda.synchronize()
     ms_per_step, kern_ms, per_launch_ms = timed_steps(step, args.steps, stream)
@@ -247,7 +285,7 @@ def bench_norm_rope(args):
     result = {
         "metric": NR_METRIC,
         "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": args.warmup_run,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"norm_rope_{w.name}", "tokens": w.tokens, "heads_q": w.hq,
@@ -274,7 +312,7 @@ def bench_norm_rope(args):
                                      w.interleaved, w.eps)
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s",
-                                  "cores": blas_threads(), "kind": "oracle",
+                                  **host_facts(), "kind": "oracle",
                                   "sample": f"full workload: {w.tokens} tokens x {w.hq}+{w.hkv} heads",
                                   "seconds": round(dt, 3)}
         err = max(float(np.abs(qo.float().cpu().numpy() - rq).max()),
@@ -314,14 +352,14 @@ def bench_cat_pad(args):
             jpa.jpa_causal_cat_pad(x, cache, c.padding, out=out, stream=stream)
 
     resolve_counts(args, step, stream)
-    for _ in range(args.warmup):
+    for _ in range(args.warmup_run):
         step()
     torch.cuda.synchronize()
     ms_per_step, kern_ms, per_step_ms = timed_steps(step, args.steps, stream)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     result = {
         "metric": CP_METRIC, "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": args.warmup_run, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "causal_conv3d_cat_pad_decoder", "shapes": [c.name for c in cases],
                    "algorithmic_bytes": nbytes},
@@ -347,6 +385,7 @@ def bench_cat_pad(args):
             del ref
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(sub_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                  "cpu_model": cpu_model(),
                                   "kind": "oracle", "seconds": round(dt, 3),
                                   "sample": "all eight shapes (time includes the bitwise comparison)"}
         result["parity"] = {"bit_exact": bool(same)}
@@ -359,7 +398,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default: at least 0.1 s of GPU work, at least 30)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps first (default: at least 0.25 s of GPU work, at least 20)")
+                    help="minimum untimed steps first (default 20); warmup always covers at "
+                         "least 0.25 s of GPU work")
     ap.add_argument("--workload", type=int, default=None)
     ap.add_argument("--op", choices=("attention", "norm_rope", "rank_share", "cat_pad"), default="attention")
     ap.add_argument("--sp", type=int, default=8, help="rank_share: ranks of the head split")
@@ -435,8 +475,8 @@ def main():
                            split_wgs=max(args.split_wgs, 0))
 
     resolve_counts(args, step, stream)
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
+    log(f"warmup {args.warmup_run} steps")
+    for _ in range(args.warmup_run):
         step()
     torch.cuda.synchronize()
 
@@ -493,7 +533,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup, "warmup_steps_run": args.warmup_run,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
