@@ -137,7 +137,7 @@ TIMED_SECONDS = 0.1
 
 def resolve_counts(args, step, stream):
     """Warmup and timed step counts from the duration of one step.  Warmup
-    always covers at least WARMUP_SECONDS of GPU work; a given --warmup is a
+    always covers at least --warmup-seconds of GPU work; a given --warmup is a
     minimum step count (default 20).  --steps is used as given, else at least
     TIMED_SECONDS of GPU work and 30 steps.  Sets args.warmup_run (the warmup
     steps actually run) and args.steps."""
@@ -151,7 +151,7 @@ def resolve_counts(args, step, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     t = max(e0.elapsed_time(e1) * 1e-3, 1e-6)
-    floor = int(np.ceil(WARMUP_SECONDS / t))
+    floor = int(np.ceil(args.warmup_seconds / t))
     args.warmup_run = max(floor, 20 if args.warmup is None else args.warmup)
     if args.warmup is None:
         args.warmup = args.warmup_run
@@ -400,6 +400,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None,
                     help="minimum untimed steps first (default 20); warmup always covers at "
                          "least 0.25 s of GPU work")
+    ap.add_argument("--warmup-seconds", type=float, default=WARMUP_SECONDS,
+                    help="least GPU time of warmup (default 0.25 s; counter runs that "
+                         "serialise every dispatch may set 0)")
     ap.add_argument("--workload", type=int, default=None)
     ap.add_argument("--op", choices=("attention", "norm_rope", "rank_share", "cat_pad"), default="attention")
     ap.add_argument("--sp", type=int, default=8, help="rank_share: ranks of the head split")

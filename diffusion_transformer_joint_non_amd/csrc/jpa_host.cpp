@@ -10,6 +10,7 @@
 
 #include "jpa.h"
 #include "jpa_params.h"
+#include "jpa_views.h"
 
 namespace {
 
@@ -95,6 +96,21 @@ jpa_status validate(const jpa_tensor* q, const jpa_tensor* k_prefix, const jpa_t
     if ((st = check_tensor(k_suffix, ts, hkv, d, true)) != JPA_OK) return st;
     if ((st = check_tensor(v_suffix, ts, hkv, d, true)) != JPA_OK) return st;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JPA_ERR_LAYOUT;
+    // Outputs share no element with the keys and values (other workgroups keep
+    // reading every key while rows are written) nor with each other.  out may
+    // be q itself, the same view: a workgroup reads only its own query rows,
+    // all of them before it writes any, and a row cut between workgroups is
+    // written by the merge launch after every piece is done.
+    const jpa_tensor* kv[4] = {k_prefix, v_prefix, k_suffix, v_suffix};
+    for (const jpa_tensor* t : kv)
+        if (!jpa_views_disjoint(out, t)) return JPA_ERR_LAYOUT;
+    if (!jpa_same_view(out, q) && !jpa_views_disjoint(out, q)) return JPA_ERR_LAYOUT;
+    if (lse) {
+        const int64_t lse_bytes = 4 * (int64_t)hq * tq;
+        const jpa_tensor* all[6] = {q, k_prefix, v_prefix, k_suffix, v_suffix, out};
+        for (const jpa_tensor* t : all)
+            if (!jpa_bytes_disjoint(lse, lse_bytes, t)) return JPA_ERR_LAYOUT;
+    }
     return JPA_OK;
 }
 
@@ -150,6 +166,12 @@ void plan_split(jpa_kernel_params& p, int wgs, bool forced, char* ws, int head_d
     p.ws_o = reinterpret_cast<float*>(ws);
     p.ws_lse = reinterpret_cast<float*>(ws + jpa_ws_o_bytes(wgs, head_dim));
 }
+
+jpa_status enqueue(const jpa_tensor* q, const jpa_tensor* k_prefix, const jpa_tensor* v_prefix,
+                   const jpa_tensor* k_suffix, const jpa_tensor* v_suffix, int32_t batch,
+                   const int32_t* cu_q, const int32_t* cu_prefix, const int32_t* cu_suffix_real,
+                   float scale, const jpa_tensor* out, float* lse, void* workspace, int wgs,
+                   bool forced, void* stream);
 
 }  // namespace
 
@@ -215,7 +237,22 @@ JPA_API jpa_status jpa_forward_ws(const jpa_tensor* q, const jpa_tensor* k_prefi
         if (workspace_bytes < jpa_ws_o_bytes(wgs, q->head_dim) + jpa_ws_lse_bytes(wgs))
             return JPA_ERR_VALUE;
     }
+    return enqueue(q, k_prefix, v_prefix, k_suffix, v_suffix, batch, cu_q, cu_prefix,
+                   cu_suffix_real, scale, out, lse, workspace, wgs, split_wgs > 0, stream);
+}
 
+}  // extern "C"
+
+namespace {
+
+// The launches of one validated forward call: one per JPA_MAX_ROWS batch
+// rows, the last round of work items cut over `wgs` key ranges through the
+// workspace `ws` when the split rule (or `forced`) says so.
+jpa_status enqueue(const jpa_tensor* q, const jpa_tensor* k_prefix, const jpa_tensor* v_prefix,
+                   const jpa_tensor* k_suffix, const jpa_tensor* v_suffix, int32_t batch,
+                   const int32_t* cu_q, const int32_t* cu_prefix, const int32_t* cu_suffix_real,
+                   float scale, const jpa_tensor* out, float* lse, void* workspace, int wgs,
+                   bool forced, void* stream) {
     jpa_kernel_params p;
     std::memset(&p, 0, sizeof(p));
     p.q = static_cast<const uint16_t*>(q->data);
@@ -267,11 +304,15 @@ JPA_API jpa_status jpa_forward_ws(const jpa_tensor* q, const jpa_tensor* k_prefi
         }
         if (p.nrows == 0) continue;
         if ((int64_t)p.total_tiles * p.hq > INT32_MAX) return JPA_ERR_SHAPE;
-        plan_split(p, wgs, split_wgs > 0, static_cast<char*>(workspace), q->head_dim);
+        plan_split(p, workspace ? wgs : 0, forced, static_cast<char*>(workspace), q->head_dim);
         if (jpa_launch_kernel(p, q->head_dim, stream) != 0) return JPA_ERR_HIP;
     }
     return JPA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 JPA_API const char* jpa_status_str(jpa_status status) {
     switch (status) {

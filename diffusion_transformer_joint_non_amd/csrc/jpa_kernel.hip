@@ -56,6 +56,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -1040,9 +1041,19 @@ int jpa_launch_kernel(const jpa_kernel_params& p, int head_dim, void* stream) {
     return (int)hipGetLastError();
 }
 
+// Compute units per device, queried once per device and kept for the life of
+// the process (hipGetDevice reads the calling thread's current device).
 int jpa_device_cus() {
-    int dev = 0, cus = 0;
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < kMaxDevices && cus > 0) cached[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }

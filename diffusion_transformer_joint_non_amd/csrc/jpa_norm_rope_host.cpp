@@ -6,6 +6,7 @@
 #include "jpa.h"
 #include "jpa_norm_rope.h"
 #include "jpa_norm_rope_params.h"
+#include "jpa_views.h"
 
 namespace {
 
@@ -21,37 +22,6 @@ jpa_status check_view(const jpa_tensor* t, int64_t tokens, int32_t heads, int32_
     if (t->head_stride < t->head_dim) return JPA_ERR_LAYOUT;
     if (t->token_stride < (int64_t)t->heads * t->head_stride) return JPA_ERR_LAYOUT;
     return JPA_OK;
-}
-
-// Element extent of a view: [data, data + span) in bf16 elements, and the
-// span of one token's row of heads.
-int64_t row_span(const jpa_tensor* t) { return (int64_t)(t->heads - 1) * t->head_stride + t->head_dim; }
-int64_t span(const jpa_tensor* t) {
-    return t->tokens == 0 ? 0 : (t->tokens - 1) * t->token_stride + row_span(t);
-}
-
-bool same_view(const jpa_tensor* a, const jpa_tensor* b) {
-    return a->data == b->data && a->tokens == b->tokens && a->heads == b->heads &&
-           a->token_stride == b->token_stride && a->head_stride == b->head_stride;
-}
-
-// True when no element of a is an element of b.  Views of one buffer with the
-// same token stride (e.g. the q and k slices of a fused QKV tensor) are
-// disjoint when their per-token column windows do not meet.
-bool disjoint(const jpa_tensor* a, const jpa_tensor* b) {
-    if (a->tokens == 0 || b->tokens == 0) return true;
-    const intptr_t pa = reinterpret_cast<intptr_t>(a->data), pb = reinterpret_cast<intptr_t>(b->data);
-    const intptr_t ea = pa + 2 * span(a), eb = pb + 2 * span(b);
-    if (ea <= pb || eb <= pa) return true;
-    if (a->token_stride != b->token_stride) return false;
-    const int64_t ts = a->token_stride;
-    int64_t d = (pb - pa) / 2;                 // element offset of b from a
-    if ((pb - pa) % 2 != 0) return false;
-    d %= ts;
-    if (d < 0) d += ts;                        // b's window starts d columns into a's token row
-    const int64_t wa = row_span(a), wb = row_span(b);
-    // windows [0, wa) and [d, d + wb) modulo ts must not intersect
-    return wa <= d && d + wb <= ts;
 }
 
 // Division by an invariant d (1 <= d <= 2^16) for dividends below 2^31:
@@ -96,11 +66,11 @@ JPA_API jpa_status jpa_qk_norm_rope(const jpa_tensor* q, const jpa_tensor* k,
     }
     // outputs: each is its own input, or shares no element with any input;
     // the two outputs share none either
-    if (!same_view(q_out, q) && !(disjoint(q_out, q) && disjoint(q_out, k))) return JPA_ERR_LAYOUT;
-    if (!same_view(k_out, k) && !(disjoint(k_out, k) && disjoint(k_out, q))) return JPA_ERR_LAYOUT;
-    if (same_view(q_out, q) && !disjoint(q_out, k)) return JPA_ERR_LAYOUT;
-    if (same_view(k_out, k) && !disjoint(k_out, q)) return JPA_ERR_LAYOUT;
-    if (!disjoint(q_out, k_out)) return JPA_ERR_LAYOUT;
+    if (!jpa_same_view(q_out, q) && !(jpa_views_disjoint(q_out, q) && jpa_views_disjoint(q_out, k))) return JPA_ERR_LAYOUT;
+    if (!jpa_same_view(k_out, k) && !(jpa_views_disjoint(k_out, k) && jpa_views_disjoint(k_out, q))) return JPA_ERR_LAYOUT;
+    if (jpa_same_view(q_out, q) && !jpa_views_disjoint(q_out, k)) return JPA_ERR_LAYOUT;
+    if (jpa_same_view(k_out, k) && !jpa_views_disjoint(k_out, q)) return JPA_ERR_LAYOUT;
+    if (!jpa_views_disjoint(q_out, k_out)) return JPA_ERR_LAYOUT;
     // rows of one tensor and token strides fit the kernel's 32-bit index math
     if (q->heads > 65536 || k->heads > 65536) return JPA_ERR_SHAPE;
     if (q->tokens * q->heads >= (int64_t(1) << 31) || q->tokens * k->heads >= (int64_t(1) << 31))

@@ -28,8 +28,10 @@
  *     out_i = sum_j exp(s_ij - LSE_i) v_j
  * Pad query slots get out = +0.0 and LSE = -inf.
  *
- * Threading / ownership: the library allocates nothing and keeps no state
- * between calls, so calls from several host threads are safe.  The caller
+ * Threading / ownership: the library allocates nothing; the only state it
+ * keeps between calls is a per-device cache of the compute-unit count, filled
+ * on first use and read atomically, so calls from several host threads are
+ * safe.  The caller
  * owns every buffer and the stream.  Every entry point validates all its
  * arguments on the host before touching the device; none throws or aborts
  * across the ABI.  All functions return a jpa_status.
@@ -59,7 +61,8 @@ typedef enum jpa_status {
     JPA_ERR_SHAPE = 3,     /* head_dim not 64/128, Hq % Hkv != 0, head counts or
                               token extents inconsistent with each other or with
                               the segment offsets                                 */
-    JPA_ERR_LAYOUT = 4,    /* misaligned pointer/stride, or overlapping rows      */
+    JPA_ERR_LAYOUT = 4,    /* misaligned pointer/stride, or an output overlapping
+                              an input or the other output                        */
     JPA_ERR_SEGMENTS = 5,  /* bad offsets: cu[0] != 0, decreasing, pad_b > Lq_b,
                               or real queries with no keys                        */
     JPA_ERR_VALUE = 6,     /* scale not finite or negative; batch < 0             */
@@ -118,6 +121,12 @@ typedef struct jpa_row_plan {
  *                  slots are never read.
  * The last pad_b query slots of row b are its pad rows (queries end with the
  * row's suffix slots); they are never read and get out = 0, LSE = -inf.
+ *
+ * The offsets are taken as host arrays only; no device copy is passed or
+ * needed.  This follows the vLLM-Omni performance-patterns guide, section on
+ * removing per-layer syncs: varlen metadata is built once on the host, so the
+ * forward never reads anything back from the device.  The host decodes each
+ * row's lengths and passes them to the kernel inside its launch arguments.
  */
 
 /*
@@ -129,9 +138,12 @@ typedef struct jpa_row_plan {
  *   scale     softmax scale (finite, >= 0; head_dim**-0.5 in every DiT above);
  *             scale*log2(e) below 1e-30 is treated as 1e-30 (uniform weights)
  *   out       [Tq, Hq, D]  bf16, written entirely (pad rows as +0.0), rounded
- *             to nearest even; must not overlap any input
+ *             to nearest even; shares no element with k_prefix, v_prefix,
+ *             k_suffix or v_suffix, and either is q itself (the same view:
+ *             in place) or shares no element with q (JPA_ERR_LAYOUT)
  *   lse       fp32 [Hq, Tq] (element (h, t) at lse[h*Tq + t]), natural log of
- *             the softmax denominator, -inf on pad rows; may be NULL
+ *             the softmax denominator, -inf on pad rows; may be NULL; shares
+ *             no byte with any tensor argument (JPA_ERR_LAYOUT)
  *   stream    a hipStream_t (NULL = the default stream)
  * D is 64 or 128; Hq % Hkv == 0.  The call is asynchronous: it validates the
  * arguments on the host, enqueues one or more kernel launches (one per 32

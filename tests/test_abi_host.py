@@ -164,6 +164,56 @@ def test_validate_rejects(mutate, code):
     assert _validate(**kw) == code
 
 
+def test_validate_output_overlap():
+    """out shares no element with K/V (other workgroups keep reading them);
+    it is q itself or disjoint from q; lse shares no byte with any tensor."""
+    bf = torch.bfloat16
+    kw = _valid_call()
+    tq, ts = kw["q"].shape[0], kw["k_suffix"].shape[0]
+    # out aliasing a K/V input
+    for name in ("k_prefix", "v_prefix", "k_suffix", "v_suffix"):
+        k2 = dict(kw)
+        src = k2[name]
+        big = torch.zeros(max(tq, src.shape[0]), 4, 64, dtype=bf)
+        k2[name] = big[:src.shape[0], :src.shape[1]]
+        k2["out"] = big[:tq]
+        assert _validate(**k2) == jpa.JPA_ERR_LAYOUT, name
+    # in place: out is q, the same view
+    k2 = dict(kw)
+    k2["out"] = k2["q"]
+    assert _validate(**k2) == jpa.JPA_OK
+    # out shifted one token against q in one buffer
+    buf = torch.zeros(tq + 1, 4, 64, dtype=bf)
+    k2 = dict(kw)
+    k2["q"], k2["out"] = buf[:-1], buf[1:]
+    assert _validate(**k2) == jpa.JPA_ERR_LAYOUT
+    # q, k, v and out as disjoint column windows of one fused buffer are fine,
+    # and the same windows overlapping by one head are not
+    fused = torch.zeros(tq, 4 + 2 + 2 + 4, 64, dtype=bf)
+    k2 = dict(kw)
+    k2["cu_suffix_real"] = [0, tq - 3, tq - 3, tq, tq]   # a layout whose suffix has tq slots
+    k2["cu_prefix"] = [0, 0, 0]
+    k2["cu_q"] = [0, tq - 3, tq]
+    k2["k_prefix"] = k2["v_prefix"] = torch.zeros(0, 2, 64, dtype=bf)
+    k2["q"], k2["k_suffix"], k2["v_suffix"], k2["out"] = (fused[:, 0:4], fused[:, 4:6],
+                                                          fused[:, 6:8], fused[:, 8:12])
+    assert _validate(**k2) == jpa.JPA_OK
+    k2["out"] = fused[:, 7:11]
+    assert _validate(**k2) == jpa.JPA_ERR_LAYOUT
+    # lse inside out, inside q, inside a K/V tensor
+    for name in ("out", "q", "k_suffix"):
+        k2 = dict(kw)
+        host = torch.zeros(k2[name].numel() * 2 + 64 + 16 * tq, dtype=torch.uint8)
+        t = host[:k2[name].numel() * 2].view(bf).view(k2[name].shape)
+        k2[name] = t
+        k2["lse"] = host[64:64 + 16 * tq].view(torch.float32).view(4, tq)
+        assert _validate(**k2) == jpa.JPA_ERR_LAYOUT, name
+    # a separate lse is fine
+    k2 = dict(kw)
+    k2["lse"] = torch.zeros(4, tq)
+    assert _validate(**k2) == jpa.JPA_OK
+
+
 def test_validate_rejects_pad_longer_than_row_and_keyless_rows():
     # pad 3 > 2 query slots
     bf = torch.bfloat16
@@ -222,10 +272,14 @@ def test_kv_token_stride_limit():
     P = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
     def check(which, stride):
-        dd = [jpa.descriptor(kw[n]) for n in ("q", "k_prefix", "v_prefix", "k_suffix", "v_suffix")]
+        # jpa_validate never dereferences tensor data: each view gets its own
+        # 1 TiB-spaced address range, so a huge stride overlaps nothing
+        dd = [jpa.descriptor(kw[n], data_ptr=(i + 1) << 40)
+              for i, n in enumerate(("q", "k_prefix", "v_prefix", "k_suffix", "v_suffix"))]
         dd[which].token_stride = stride
+        o = jpa.descriptor(kw["out"], data_ptr=6 << 40)
         return lib.jpa_validate(*[ctypes.byref(x) for x in dd], 2, P(cq), P(cp), P(cs), 0.1,
-                                ctypes.byref(od), None)
+                                ctypes.byref(o), None)
 
     for which in (1, 2, 3, 4):
         assert check(which, (1 << 23) - 8) == jpa.JPA_OK

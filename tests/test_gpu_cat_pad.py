@@ -84,10 +84,14 @@ def test_decoder_shapes(case):
     x, cache = _dev(inp["x"]), _dev(inp["cache"]) if case.cache_frames else None
     out = jpa.jpa_causal_cat_pad(x, cache, case.padding)
     torch.cuda.synchronize()
-    chans = [0, case.c - 1]
-    ref = oracle.cat_pad(inp["x"][:, chans], inp["cache"][:, chans] if case.cache_frames else None, case.padding)
-    got = _host_bits(out[:, chans].contiguous())
-    assert got.shape == ref.shape and np.array_equal(got, ref)
+    # every channel, bit for bit, in blocks of 32 channels to bound host memory
+    for c0 in range(0, case.c, 32):
+        c1 = min(case.c, c0 + 32)
+        ref = oracle.cat_pad(inp["x"][:, c0:c1], inp["cache"][:, c0:c1] if case.cache_frames else None,
+                             case.padding)
+        got = _host_bits(out[:, c0:c1].contiguous())
+        assert got.shape == ref.shape and np.array_equal(got, ref), (case.name, c0)
+        del ref, got
 
 
 def test_output_fully_written():

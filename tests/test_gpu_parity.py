@@ -128,17 +128,9 @@ def test_pad_contents_are_never_read(case):
         assert np.array_equal(res[0][1].view(np.int32), b[1].view(np.int32))
 
 
-def test_split_equals_concat():
-    """Same keys given as prefix+suffix or as one suffix give the same
-    attention (sglang PR #26973 review: non-SP branches concatenate then
-    attend).  The kernel's key order depends on how the keys are split (the
-    partial 64-key runs of each tensor go first), so the two runs differ only
-    by rounding (accumulation order and the bf16 rounding of weights taken
-    against a different running reference): both meet the oracle bar, and
-    they agree within 4e-3 max / 5e-5 mean on outputs and 1e-5 on the LSE."""
-    w = synth.custom_workload(4, 4, 128, [77, 512], [819, 190], [2, 70], "prefix+suffix", wid=610)
-    x = synth.make_inputs(w, pad_fill="garbage")
-    o1, l1 = gh.run(x)
+def _as_one_suffix(w, x):
+    """The same call with each row's prefix and suffix keys concatenated into
+    one suffix (pad slots kept at the row's end) and no prefix."""
     ks, vs, cs = [], [], [0]
     p_off = s_off = 0
     for b in range(w.batch):
@@ -152,7 +144,41 @@ def test_split_equals_concat():
     x2.update(k_prefix=x["k_prefix"][:0], v_prefix=x["v_prefix"][:0], k_suffix=np.concatenate(ks),
               v_suffix=np.concatenate(vs), cu_prefix=np.zeros(w.batch + 1, np.int32),
               cu_suffix_real=np.asarray(cs, np.int32))
-    o2, l2 = gh.run(x2)
+    return x2
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_split_equals_concat_bitwise_when_prefixes_fill_tiles(d):
+    """With every prefix length a multiple of the 64-key tile, the split walk
+    and the walk over the concatenated keys visit the same keys in the same
+    order (the R mod 64 leftover suffix keys first, then the prefix tiles,
+    then the suffix tiles), so the outputs and LSE are bit-identical (sglang
+    PR #26973 review: without sequence parallelism the layer concatenates the
+    prefix and suffix, then attends)."""
+    w = synth.custom_workload(4, 2, d, [64, 512, 0, 128], [819, 190, 300, 64], [2, 70, 0, 5],
+                              "prefix+suffix", wid=611)
+    x = synth.make_inputs(w, pad_fill="garbage")
+    o1, l1 = gh.run(x)
+    o2, l2 = gh.run(_as_one_suffix(w, x))
+    oh, lh = gh.host(o1, l1)
+    gh.assert_parity_full(w, x, oh, lh)
+    assert np.array_equal(gh.bits(o1), gh.bits(o2))
+    assert np.array_equal(l1.cpu().numpy().view(np.int32), l2.cpu().numpy().view(np.int32))
+
+
+def test_split_equals_concat():
+    """Same keys given as prefix+suffix or as one suffix give the same
+    attention (sglang PR #26973 review: non-SP branches concatenate then
+    attend).  With ragged prefixes the kernel's key order depends on how the
+    keys are split (the partial 64-key runs of each tensor go first), so the
+    two runs differ only by rounding (accumulation order and the bf16
+    rounding of weights taken against a different running reference): both
+    meet the oracle bar, and they agree within 4e-3 max / 5e-5 mean on
+    outputs and 1e-5 on the LSE."""
+    w = synth.custom_workload(4, 4, 128, [77, 512], [819, 190], [2, 70], "prefix+suffix", wid=610)
+    x = synth.make_inputs(w, pad_fill="garbage")
+    o1, l1 = gh.run(x)
+    o2, l2 = gh.run(_as_one_suffix(w, x))
     for o, l in ((o1, l1), (o2, l2)):
         oh, lh = gh.host(o, l)
         gh.assert_parity_full(w, x, oh, lh)
@@ -188,6 +214,34 @@ def test_strided_views_match_contiguous():
     o3, _ = gh.run(x, dev=dev, out=big[:, :, :d])
     assert np.array_equal(gh.bits(o1), gh.bits(o3))
     assert torch.count_nonzero(big[:, :, d:]) == 0
+
+
+@pytest.mark.parametrize("split", [None, 0, 7])
+def test_in_place_output_over_q(split):
+    """out may be q itself: a workgroup reads only its own query rows, all
+    before writing, and rows cut between key ranges are written by the merge
+    launch.  The in-place result equals the out-of-place one bit for bit
+    (jpa_forward, and jpa_forward_ws automatic and forced over 7 ranges)."""
+    w = synth.custom_workload(6, 2, 128, [77, 128], [1000, 300], [13, 40], "prefix+suffix", wid=625)
+    x = synth.make_inputs(w, pad_fill="garbage")
+    dev = gh.device_inputs(x)
+
+    def call(q, out):
+        if split is None:
+            return jpa.jpa_forward(q, dev["k_prefix"], dev["v_prefix"], dev["k_suffix"], dev["v_suffix"],
+                                   x["cu_q"], x["cu_prefix"], x["cu_suffix_real"], x["scale"], out=out)
+        return jpa.jpa_forward_ws(q, dev["k_prefix"], dev["v_prefix"], dev["k_suffix"], dev["v_suffix"],
+                                  x["cu_q"], x["cu_prefix"], x["cu_suffix_real"], x["scale"], out=out,
+                                  split_wgs=split)
+
+    o1, l1 = call(dev["q"], None)
+    q2 = dev["q"].clone()
+    o2, l2 = call(q2, q2)
+    torch.cuda.synchronize()
+    assert o2.data_ptr() == q2.data_ptr()
+    assert np.array_equal(gh.bits(o1), gh.bits(o2))
+    assert np.array_equal(l1.cpu().numpy().view(np.int32), l2.cpu().numpy().view(np.int32))
+    gh.assert_parity_full(w, x, *gh.host(o2, l2))
 
 
 def test_deterministic_and_guard_bytes():
