@@ -24,7 +24,7 @@ LIB = os.path.join(LIB_DIR, "libjpa.so")
 STRICT_LIB = os.path.join(LIB_DIR, "libjpa_strict_waits.so")
 ARCH = "gfx950"
 
-SOURCES = ["jpa_kernel.hip", "jpa_host.cpp", "jpa_norm_rope.hip", "jpa_norm_rope_host.cpp",
+SOURCES = ["jpa_kernel.hip", "jpa_scratch.hip", "jpa_host.cpp", "jpa_norm_rope.hip", "jpa_norm_rope_host.cpp",
            "jpa_shard_host.cpp", "jpa_cat_pad.hip", "jpa_cat_pad_host.cpp"]
 
 HIPCC_FLAGS = [

@@ -10,6 +10,7 @@
 
 #include "jpa.h"
 #include "jpa_params.h"
+#include "jpa_scratch.h"
 #include "jpa_views.h"
 
 namespace {
@@ -241,6 +242,31 @@ JPA_API jpa_status jpa_forward_ws(const jpa_tensor* q, const jpa_tensor* k_prefi
                    cu_suffix_real, scale, out, lse, workspace, wgs, split_wgs > 0, stream);
 }
 
+JPA_API jpa_status jpa_forward_scratch(const jpa_tensor* q, const jpa_tensor* k_prefix,
+                                       const jpa_tensor* v_prefix, const jpa_tensor* k_suffix,
+                                       const jpa_tensor* v_suffix, int32_t batch,
+                                       const int32_t* cu_q, const int32_t* cu_prefix,
+                                       const int32_t* cu_suffix_real, float scale,
+                                       const jpa_tensor* out, float* lse, int32_t split_wgs,
+                                       void* stream) {
+    jpa_status st = validate(q, k_prefix, v_prefix, k_suffix, v_suffix, batch, cu_q, cu_prefix,
+                             cu_suffix_real, scale, out, lse);
+    if (st != JPA_OK) return st;
+    if (split_wgs < 0) return JPA_ERR_VALUE;
+    if (split_wgs > JPA_SCRATCH_MAX_WGS) return JPA_ERR_SCRATCH;
+    int wgs = split_wgs;
+    if (wgs == 0 && device_cus(&wgs) != JPA_OK) return JPA_ERR_HIP;
+    if (wgs > JPA_SCRATCH_MAX_WGS) return JPA_ERR_SCRATCH;
+    // the scratch of JPA_SCRATCH_MAX_WGS ranges at head_dim 128 holds any
+    // smaller request
+    if (jpa_ws_o_bytes(wgs, q->head_dim) + jpa_ws_lse_bytes(wgs) > jpa_scratch_bytes())
+        return JPA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (jpa_scratch_address(&ws) != 0) return JPA_ERR_HIP;
+    return enqueue(q, k_prefix, v_prefix, k_suffix, v_suffix, batch, cu_q, cu_prefix,
+                   cu_suffix_real, scale, out, lse, ws, wgs, split_wgs > 0, stream);
+}
+
 }  // extern "C"
 
 namespace {
@@ -324,6 +350,8 @@ JPA_API const char* jpa_status_str(jpa_status status) {
         case JPA_ERR_SEGMENTS: return "JPA_ERR_SEGMENTS: invalid segment offsets";
         case JPA_ERR_VALUE: return "JPA_ERR_VALUE: scale must be finite and >= 0, batch >= 0";
         case JPA_ERR_HIP: return "JPA_ERR_HIP: the HIP runtime rejected the launch";
+        case JPA_ERR_SCRATCH:
+            return "JPA_ERR_SCRATCH: more key ranges than the static scratch holds (JPA_SCRATCH_MAX_WGS)";
     }
     return "JPA_ERR_UNKNOWN";
 }

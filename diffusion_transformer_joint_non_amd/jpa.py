@@ -27,10 +27,12 @@ JPA_ERR_LAYOUT = 4
 JPA_ERR_SEGMENTS = 5
 JPA_ERR_VALUE = 6
 JPA_ERR_HIP = 7
+JPA_ERR_SCRATCH = 8
+SCRATCH_MAX_WGS = 256  # JPA_SCRATCH_MAX_WGS
 JPA_DTYPE_BF16 = 1
 BLOCK_M = 256          # query rows per workgroup (for launch accounting only)
 
-EXPORTED = ("jpa_forward", "jpa_forward_ws", "jpa_workspace_bytes", "jpa_validate", "jpa_plan",
+EXPORTED = ("jpa_forward", "jpa_forward_ws", "jpa_forward_scratch", "jpa_workspace_bytes", "jpa_validate", "jpa_plan",
             "jpa_status_str", "jpa_abi_version", "jpa_qk_norm_rope", "jpa_shard_plan",
             "jpa_tail_attn_meta", "jpa_tail_segments", "jpa_causal_cat_pad")
 
@@ -116,6 +118,10 @@ def _open(path: str) -> ctypes.CDLL:
     lib.jpa_forward_ws.argtypes = [tp, tp, tp, tp, tp, ctypes.c_int32, i32p, i32p, i32p,
                                    ctypes.c_float, tp, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]
+    lib.jpa_forward_scratch.restype = ctypes.c_int
+    lib.jpa_forward_scratch.argtypes = [tp, tp, tp, tp, tp, ctypes.c_int32, i32p, i32p, i32p,
+                                        ctypes.c_float, tp, ctypes.c_void_p, ctypes.c_int32,
+                                        ctypes.c_void_p]
     lib.jpa_workspace_bytes.restype = ctypes.c_size_t
     lib.jpa_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
     lib.jpa_validate.restype = ctypes.c_int
@@ -286,6 +292,27 @@ def jpa_forward_ws(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix, c
                             float(scale), ctypes.byref(od),
                             None if lse is None else ctypes.c_void_p(lse.data_ptr()),
                             ws_ptr, ws_bytes, int(split_wgs), ctypes.c_void_p(handle))
+    _raise_for(st)
+    return out, lse
+
+
+def jpa_forward_scratch(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix, cu_suffix_real,
+                        scale: float, out, lse=None, stream=None, split_wgs: int = 0):
+    """jpa_forward_ws with the library's static device scratch in place of a
+    workspace: the C call allocates nothing (for callers that cannot).  out
+    (and lse, if wanted) must be given.  Calls that may overlap on one device
+    race on the shared scratch.  Returns (out, lse)."""
+    lib = load_library()
+    if out is None:
+        raise ValueError("jpa_forward_scratch writes into a given out (it allocates nothing)")
+    cq, cp, cs, batch, d = _common(q, k_prefix, v_prefix, k_suffix, v_suffix, cu_q, cu_prefix,
+                                   cu_suffix_real)
+    out, lse, handle = _prepare(q, out, lse, False, stream)
+    od = descriptor(out)
+    st = lib.jpa_forward_scratch(*[ctypes.byref(x) for x in d], batch, _i32p(cq), _i32p(cp), _i32p(cs),
+                                 float(scale), ctypes.byref(od),
+                                 None if lse is None else ctypes.c_void_p(lse.data_ptr()),
+                                 int(split_wgs), ctypes.c_void_p(handle))
     _raise_for(st)
     return out, lse
 

@@ -66,8 +66,10 @@ typedef enum jpa_status {
     JPA_ERR_SEGMENTS = 5,  /* bad offsets: cu[0] != 0, decreasing, pad_b > Lq_b,
                               or real queries with no keys                        */
     JPA_ERR_VALUE = 6,     /* scale not finite or negative; batch < 0             */
-    JPA_ERR_HIP = 7        /* the HIP runtime rejected the launch (no device,
+    JPA_ERR_HIP = 7,       /* the HIP runtime rejected the launch (no device,
                               no gfx950 code object, bad stream, ...)             */
+    JPA_ERR_SCRATCH = 8    /* jpa_forward_scratch: more key ranges than its
+                              static scratch holds (JPA_SCRATCH_MAX_WGS)          */
 } jpa_status;
 
 typedef enum jpa_dtype {
@@ -201,6 +203,39 @@ JPA_API jpa_status jpa_forward_ws(const jpa_tensor* q,
                                   const jpa_tensor* out, float* lse,
                                   void* workspace, size_t workspace_bytes, int32_t split_wgs,
                                   void* stream);
+
+/*
+ * jpa_forward_scratch -- jpa_forward_ws for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same launches, with the cut items' partial
+ * results in a static device array of the library instead of a caller
+ * workspace.  No allocation of any kind is made by this call.
+ *
+ *   split_wgs  as in jpa_forward_ws (0: the device's compute units, cut only
+ *              when the split rule says so; > 0: that many ranges, always
+ *              cut); at most JPA_SCRATCH_MAX_WGS.
+ * The array holds the workspace of JPA_SCRATCH_MAX_WGS ranges at head_dim 128
+ * (64.5 MiB); every device the library runs on keeps its own copy until the
+ * process ends.  Nothing in it needs to start at zero.  All calls on one
+ * device share it, so two calls that may run at the same time on one device
+ * (different streams without ordering between them) race and corrupt each
+ * other's results; calls on one stream are ordered and safe.  Results equal
+ * jpa_forward_ws's with the same split_wgs, bit for bit.
+ * Errors as jpa_forward_ws, plus JPA_ERR_SCRATCH when split_wgs (or, for 0,
+ * the device's compute units) exceeds JPA_SCRATCH_MAX_WGS; JPA_ERR_HIP when
+ * the device or the array's address cannot be queried.
+ */
+#define JPA_SCRATCH_MAX_WGS 256
+JPA_API jpa_status jpa_forward_scratch(const jpa_tensor* q,
+                                       const jpa_tensor* k_prefix, const jpa_tensor* v_prefix,
+                                       const jpa_tensor* k_suffix, const jpa_tensor* v_suffix,
+                                       int32_t batch,
+                                       const int32_t* cu_q, const int32_t* cu_prefix,
+                                       const int32_t* cu_suffix_real,
+                                       float scale,
+                                       const jpa_tensor* out, float* lse,
+                                       int32_t split_wgs,
+                                       void* stream);
 
 /*
  * jpa_workspace_bytes -- workspace size jpa_forward_ws needs for head_dim

@@ -55,7 +55,7 @@ def test_strict_waits_build_exports_the_same_symbols():
 def test_abi_version_and_status_strings():
     m = re.search(r"#define JPA_ABI_VERSION (\d+)", open(HEADER).read())
     assert jpa.jpa_abi_version() == int(m.group(1))
-    for code in range(8):
+    for code in range(9):
         s = jpa.jpa_status_str(code)
         assert s.startswith("JPA_")
     assert jpa.jpa_status_str(99) == "JPA_ERR_UNKNOWN"
@@ -259,6 +259,34 @@ def test_null_pointers_and_bad_counts_from_c():
     assert lib.jpa_plan(2, P(cq), P(cp), P(cs), 4, 64, None, None) == 0
     bad = np.asarray([0, 7, 6, 10, 12], np.int32)
     assert lib.jpa_plan(2, P(cq), P(cp), P(bad), 4, 64, None, None) == jpa.JPA_ERR_SEGMENTS
+
+
+def test_scratch_entry_checks_before_the_device():
+    """jpa_forward_scratch validates like jpa_forward and rejects a split
+    over more key ranges than its static scratch holds, on the host, before
+    any device query (so these statuses come back on a machine without a
+    GPU as well)."""
+    lib = jpa.load_library()
+    kw = _valid_call()
+    d = [jpa.descriptor(kw[n]) for n in ("q", "k_prefix", "v_prefix", "k_suffix", "v_suffix")]
+    od = jpa.descriptor(kw["out"])
+    cq, cp, cs = (np.asarray(kw[n], np.int32) for n in ("cu_q", "cu_prefix", "cu_suffix_real"))
+    P = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def call(wgs, scale=0.1, lse=None):
+        return lib.jpa_forward_scratch(*[ctypes.byref(x) for x in d], 2, P(cq), P(cp), P(cs), scale,
+                                       ctypes.byref(od), lse, wgs, None)
+
+    assert call(jpa.SCRATCH_MAX_WGS + 1) == jpa.JPA_ERR_SCRATCH
+    assert call(1 << 30) == jpa.JPA_ERR_SCRATCH
+    assert call(-1) == jpa.JPA_ERR_VALUE
+    assert call(8, scale=float("nan")) == jpa.JPA_ERR_VALUE          # argument errors first
+    assert call(jpa.SCRATCH_MAX_WGS + 1, scale=-1.0) == jpa.JPA_ERR_VALUE
+    assert "JPA_SCRATCH_MAX_WGS" in jpa.jpa_status_str(jpa.JPA_ERR_SCRATCH)
+    m = re.search(r"#define JPA_SCRATCH_MAX_WGS (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == jpa.SCRATCH_MAX_WGS
+    if not torch.cuda.is_available():
+        assert call(8) == jpa.JPA_ERR_HIP
 
 
 def test_kv_token_stride_limit():
