@@ -493,7 +493,7 @@ def main():
     # Launch-bound sizes: the per-call time when the host is out of the way,
     # from a HIP graph of 20 calls replayed (the library allocates nothing and
     # never synchronises, so its calls capture as they are).
-    graph_us = None
+    graph_us = prepared_us = None
     if kern_ms < 1.0:
         g = torch.cuda.CUDAGraph()
         cs = torch.cuda.Stream()
@@ -523,6 +523,21 @@ def main():
         g1.record()
         torch.cuda.synchronize()
         graph_us = g0.elapsed_time(g1) * 1e3 / (n_timed * 20)
+        # the same call eagerly, its arguments marshalled once (PreparedForward)
+        call = jpa.prepare_forward(dev["q"], dev["k_prefix"], dev["v_prefix"], dev["k_suffix"],
+                                   dev["v_suffix"], x["cu_q"], x["cu_prefix"], x["cu_suffix_real"],
+                                   x["scale"], out=out, lse=lse, stream=stream,
+                                   workspace=None if args.split_wgs < 0 else "auto",
+                                   split_wgs=max(args.split_wgs, 0))
+        n_calls = max(100, int(np.ceil(TIMED_SECONDS / (kern_ms * 1e-3))))
+        for _ in range(n_calls):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_calls):
+            call()
+        torch.cuda.synchronize()
+        prepared_us = (time.perf_counter() - t0) * 1e6 / n_calls
     # minimum bytes a call moves: real q read, every out slot written, each
     # row's real prefix/suffix K and V read once, lse written
     real_q = int(sum(r[2] for r in rows))
@@ -561,7 +576,8 @@ def main():
                      "algorithmic_bytes": algo_bytes,
                      "hbm_gbs_algorithmic": round(algo_bytes / (kern_ms * 1e-3) / 1e9, 1),
                      "us_per_call": round(kern_ms * 1e3, 2),
-                     "us_per_call_graph": None if graph_us is None else round(graph_us, 2)},
+                     "us_per_call_graph": None if graph_us is None else round(graph_us, 2),
+                     "us_per_call_prepared": None if prepared_us is None else round(prepared_us, 2)},
     }
 
     if not args.no_cpu_baseline:

@@ -289,6 +289,28 @@ def test_scratch_entry_checks_before_the_device():
         assert call(8) == jpa.JPA_ERR_HIP
 
 
+def test_prepared_forward_validates_once_and_reaches_the_launch():
+    """PreparedForward marshals the arguments once; a bad call is rejected at
+    construction, a good one reaches the launch (JPA_ERR_HIP without a GPU)."""
+    kw = _valid_call()
+    args = [kw[n] for n in ("q", "k_prefix", "v_prefix", "k_suffix", "v_suffix", "cu_q", "cu_prefix",
+                            "cu_suffix_real", "scale")]
+    lse = torch.zeros(4, kw["q"].shape[0])
+    call = jpa.prepare_forward(*args, out=kw["out"], lse=lse, workspace=None, stream=0)
+    assert call.out is kw["out"] and call.lse is lse
+    if not torch.cuda.is_available():
+        with pytest.raises(jpa.JpaError) as e:
+            call()
+        assert e.value.status == jpa.JPA_ERR_HIP
+    bad = list(args)
+    bad[8] = float("nan")
+    with pytest.raises(jpa.JpaArgumentError):
+        jpa.prepare_forward(*bad, out=kw["out"], lse=lse, workspace=None, stream=0)
+    with pytest.raises(jpa.JpaArgumentError):
+        jpa.prepare_forward(*args, out=kw["q"][:, :2],
+                            workspace=None, stream=0, with_lse=False)
+
+
 def test_kv_token_stride_limit():
     # K/V rows are addressed with a 24-bit multiply of the byte stride: token
     # strides of 2^23 elements or more are rejected (only for K/V tensors).

@@ -244,6 +244,26 @@ def test_in_place_output_over_q(split):
     gh.assert_parity_full(w, x, *gh.host(o2, l2))
 
 
+def test_prepared_call_matches_and_rereads_its_inputs():
+    """A PreparedForward call equals jpa_forward_ws bit for bit, and a later
+    call reads the tensors' current contents (the arguments were marshalled
+    once, the data is not cached)."""
+    w = synth.custom_workload(6, 2, 128, [77, 128], [1000, 300], [13, 40], "prefix+suffix", wid=626)
+    x = synth.make_inputs(w, pad_fill="garbage")
+    dev = gh.device_inputs(x)
+    args = [dev[n] for n in gh.NAMES] + [x["cu_q"], x["cu_prefix"], x["cu_suffix_real"], x["scale"]]
+    call = jpa.prepare_forward(*args)
+    for rep in range(2):
+        o1, l1 = call()
+        o2, l2 = jpa.jpa_forward_ws(*args)
+        torch.cuda.synchronize()
+        assert np.array_equal(gh.bits(o1), gh.bits(o2)), rep
+        assert np.array_equal(l1.cpu().numpy().view(np.int32), l2.cpu().numpy().view(np.int32)), rep
+        if rep == 0:
+            gh.assert_parity_full(w, x, *gh.host(o1, l1))
+            dev["q"].mul_(-1.0)                    # new contents, same storage
+
+
 def test_deterministic_and_guard_bytes():
     w = synth.custom_workload(6, 2, 128, [77], [1000], [13], "prefix+suffix", wid=630)
     x = synth.make_inputs(w)
