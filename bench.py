@@ -192,6 +192,45 @@ def host_facts():
             "cpu_model": cpu_model()}
 
 
+def _read(path):
+    try:
+        with open(path) as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
+def _git_head():
+    root = os.path.dirname(os.path.abspath(__file__))
+    head = _read(os.path.join(root, ".git", "HEAD"))
+    if head and head.startswith("ref: "):
+        return _read(os.path.join(root, ".git", head[5:]))
+    return head
+
+
+def _sclk_levels_mhz():
+    """DPM levels of the GPU clock (MHz) from sysfs, or None where hidden."""
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        txt = _read(f)
+        if txt:
+            return [int(t.split()[1].lower().rstrip("mhz")) for t in txt.splitlines() if len(t.split()) > 1
+                    and t.split()[1].lower().endswith("mhz")]
+    return None
+
+
+def descriptor(seed_base):
+    """Frozen description of where and on what the line was measured: code
+    revision, input seeds, software stack and the device."""
+    import torch
+    prop = torch.cuda.get_device_properties(0)
+    return {"git": _git_head(), "kernel_source_sha256_16": kernel_source_hash(), "input_seed_base": seed_base,
+            "rocm": _read("/opt/rocm/.info/version"), "hip_runtime": torch.version.hip,
+            "torch": torch.__version__, "amdgpu_driver": _read("/sys/module/amdgpu/version"),
+            "gpu": prop.name, "arch": prop.gcnArchName, "compute_units": prop.multi_processor_count,
+            "sclk_levels_mhz": _sclk_levels_mhz()}
+
+
 # Above this much valid work the oracle runs on a seeded random subset of
 # 4096 real query rows per head (every head, every real key) instead of the
 # whole workload: the two largest workloads.
@@ -580,6 +619,7 @@ def main():
                      "us_per_call_prepared": None if prepared_us is None else round(prepared_us, 2)},
     }
 
+    result["descriptor"] = descriptor(1000 * w.wid)
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the fp64 oracle on the host")
         base, ref_o, ref_l, sub = cpu_baseline(w, x, flops)

@@ -46,3 +46,18 @@ def test_committed_profiles_name_the_sources_they_cover():
         h = r["kernel_source_sha256_16"]
         assert len(h) == 16 and int(h, 16) >= 0, f
         assert r["hbm_bytes_per_launch"] > 0, f
+
+
+def test_git_head_follows_a_symbolic_ref(tmp_path, monkeypatch):
+    """The descriptor's revision: HEAD's ref resolved to its commit id, or
+    None where no repository metadata travels with the tree."""
+    git = tmp_path / ".git"
+    (git / "refs" / "heads").mkdir(parents=True)
+    (git / "HEAD").write_text("ref: refs/heads/main\n")
+    (git / "refs" / "heads" / "main").write_text("0123abcd" * 5 + "\n")
+    monkeypatch.setattr(bench.os.path, "abspath", lambda p: str(tmp_path / "bench.py"))
+    assert bench._git_head() == "0123abcd" * 5
+    (git / "HEAD").write_text("fedc" * 10 + "\n")          # detached
+    assert bench._git_head() == "fedc" * 10
+    monkeypatch.setattr(bench.os.path, "abspath", lambda p: str(tmp_path / "sub" / "bench.py"))
+    assert bench._git_head() is None
