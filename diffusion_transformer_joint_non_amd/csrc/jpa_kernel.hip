@@ -88,10 +88,32 @@ static_assert(kBM == JPA_BLOCK_M, "host and kernel tile height differ");
 __device__ __forceinline__ int perm_k(int i) {
     return (i & 0x13) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
-// 16-byte chunk swizzle of K rows: the rows perm_k(0..15) read by lanes 0..15
-// of a half get 0..15, distinct modulo 8 within each group of 8 lanes.
-__device__ __forceinline__ int swz_k(int row) {
-    return (row & 3) | (((row >> 3) & 1) << 2) | (((row >> 2) & 1) << 3);
+// LDS tile layout.  A K or V tile is copied by wave-wide 16-byte-per-lane
+// loads, each filling one block of 512 / D consecutive key rows (1 KB); the
+// blocks sit kBlockPad elements (16 bytes) apart.  The pad moves each block
+// by one 16-byte bank group, so a chunk's bank group is (block + position)
+// mod 16, and the swizzle below only has to separate the rows inside one
+// block.  That keeps a lane's copy offsets the same for every block of a
+// tile: one voffset and one m0 per tensor and tile, the blocks told apart by
+// the instruction offset (LDS) and the scalar offset (global memory).
+constexpr int kBlockPad = 8;
+template <int D>
+__host__ __device__ constexpr int row_elems(int r) {      // element offset of tile row r
+    constexpr int kRowsPerBlock = 512 / D;
+    return (r / kRowsPerBlock) * (kRowsPerBlock * D + kBlockPad) + (r % kRowsPerBlock) * D;
+}
+// 16-byte chunk c of K row r sits at position k_pos(c, r) of its LDS row (an
+// XOR, so the same function gives the chunk a copy lane fetches for a
+// position).  D = 128 (4 rows a block): the row's block position a moves bits
+// 2-3 of the position; a read by 16 lanes of 16 rows (4 blocks x 4 positions)
+// then lands in 16 distinct bank groups.  D = 64 (8 rows a block): bits 1-2
+// by a / 2; the 16 rows of a read (2 blocks, rows of 128 bytes) again fill
+// 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int k_pos(int c, int r) {
+    constexpr int kRowsPerBlock = 512 / D;
+    const int a = r % kRowsPerBlock;
+    return (c ^ (D == 128 ? 4 * a : (a & 6))) & (D / 8 - 1);
 }
 
 // V tiles: the 16-byte chunk c of key row r sits at chunk v_pos(c, r) of
@@ -152,18 +174,30 @@ __device__ __forceinline__ void lds_copy16(const void* gaddr, const void* lds_ds
 __device__ __forceinline__ u32x4_t make_rsrc(uintptr_t base, uint32_t num_records) {
     return u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, num_records, 0x00020000u};
 }
-// 16-byte-per-lane buffer -> LDS copy (buffer_load_dwordx4 ... lds) at a
-// 32-bit per-lane offset; untracked like lds_copy16.  The LDS address is
-// lds_base + OFF (bytes), formed in m0 inside the asm so that only lds_base
-// occupies a scalar register.
+__device__ __forceinline__ u32x4_t uniform_rsrc(u32x4_t r) {
+    return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane(r[0]), (uint32_t)__builtin_amdgcn_readfirstlane(r[1]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(r[2]), (uint32_t)__builtin_amdgcn_readfirstlane(r[3])};
+}
+// 16-byte-per-lane buffer -> LDS copies (buffer_load_dwordx4 ... lds);
+// untracked like lds_copy16.  Lane l lands at LDS byte m0 + OFF + 16 l and
+// reads global memory at base + soff + voff + OFF.  A run of copies shares
+// one m0: the first sets it (lds_base + M0OFF, with the wait state a DMA
+// needs after an m0 write) and hands it out, the rest take it back in, each
+// placed by its own OFF (below 4096) and a soff that subtracts OFF again.
+template <int M0OFF>
+__device__ __forceinline__ uint32_t lds_copy16_buf_m0(u32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+    uint32_t m0_out;
+    asm volatile("s_add_u32 m0, %4, %5\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 : "={m0}"(m0_out)
+                 : "v"(voff), "s"(uniform_rsrc(rsrc)), "s"(soff), "s"(lds_base), "n"(M0OFF)
+                 : "memory", "scc");
+    return m0_out;
+}
 template <int OFF>
-__device__ __forceinline__ void lds_copy16_buf(u32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
-    rsrc = u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
-                   (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
-    uint32_t m0_out;       // m0 is written here: an output, so nothing else is kept in it
-    asm volatile("s_add_u32 m0, %3, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 : "={m0}"(m0_out) : "v"(voff), "s"(rsrc), "s"(lds_base), "n"(OFF) : "memory", "scc");
-    (void)m0_out;
+__device__ __forceinline__ void lds_copy16_buf_at(u32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t m0v) {
+    static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%4 lds"
+                 :: "v"(voff), "s"(uniform_rsrc(rsrc)), "s"(soff), "{m0}"(m0v), "n"(OFF) : "memory");
 }
 
 // A wave-uniform 64-bit value in scalar registers.
@@ -230,7 +264,8 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     constexpr int kDS = D / 16;              // 16-wide k-steps of QK^T
     constexpr int kDB = D / 32;              // 32-row blocks of O^T
     constexpr int kCH = D / 8;               // 16-byte chunks per K/V row
-    constexpr int kTile = kBN * D;           // elements of one K or V tile
+    constexpr int kBlockElems = 512 + kBlockPad;     // one copy block (512 / D rows) and its pad
+    constexpr int kTile = kBN / (512 / D) * kBlockElems;   // elements of one K or V tile buffer
     constexpr int kRowsPerOp = 512 / D;      // rows filled by one wave-wide 16 B/lane load
     constexpr int kOpsPerWave = kBN / kRowsPerOp / kWaves;
     constexpr int kXSlots = kDS * kQB;       // QK MFMAs per 32-key unit
@@ -259,6 +294,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     };
     // Four K and four V tile buffers.  The tile copies are untracked inline
     // asm, so no compiler-inserted wait depends on how they are laid out.
+    static_assert(kBM / kWaves * D <= kTile, "a wave stages its output rows in one K tile buffer");
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[4 * kTile];
     __shared__ __attribute__((aligned(16))) uint16_t lds_v[4 * kTile];
     auto kbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint16_t* {
@@ -443,36 +479,35 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         const int64_t ts = s_row0 + (int64_t)Rf * kBN + (pi - headP);
         const uint16_t* gk = pre ? kp + tp * kp_ts : ks + ts * ks_ts;
         const uint16_t* gv = pre ? vp + tp * vp_ts : vs + ts * vs_ts;
-        lds_copy16(gk + ((pc ^ swz_k(row)) & (kCH - 1)) * 8, kbuf(SLOT) + row0 * D);
-        lds_copy16(gv + v_chunk_at<D>(pc, row) * 8, vbuf(SLOT) + row0 * D);
+        lds_copy16(gk + k_pos<D>(pc, row) * 8, kbuf(SLOT) + row_elems<D>(row0));
+        lds_copy16(gv + v_chunk_at<D>(pc, row) * 8, vbuf(SLOT) + row_elems<D>(row0));
     };
-    //  Full tiles: a buffer resource whose base is the tile's row 0 plus a
-    //  32-bit per-lane offset (row * token stride + chunk), fixed per tensor.
-    //  The loop advances the base by 64 rows per tile and switches tensor once;
-    //  its look-ahead past the last tile uses an empty resource (every lane
-    //  out of range: nothing is read, zeros land in a buffer nobody reads).
+    //  Full tiles: a buffer resource whose base is the tile's row 0 (less
+    //  kCopyBias bytes), one per-lane offset per tensor (the lane's row in its
+    //  block times the token stride, plus its chunk), and per op a scalar
+    //  offset: op i of a wave fills block (wave * kOpsPerWave + i), so its
+    //  rows start i * kRowsPerOp rows further on, and it carries the
+    //  instruction offset i * kBlockBytes, which the scalar offset takes back
+    //  off the global address.  The loop advances the base by 64 rows per
+    //  tile and switches tensor once; its look-ahead past the last tile uses
+    //  an empty resource (every lane out of range: nothing is read, zeros
+    //  land in a buffer nobody reads).
+    constexpr int kBlockBytes = 2 * kBlockElems;
+    // Keeps every scalar offset non-negative: token strides are at least D
+    // elements, so a block's rows span at least 1024 bytes of global memory.
+    constexpr uint32_t kCopyBias = 64;
+    static_assert((kOpsPerWave - 1) * (kBlockBytes - 1024) <= (int)kCopyBias, "scalar offsets stay non-negative");
     const int lane_row = lane / kCH;
     const int lane_pc = lane % kCH;
-    int r_lane[kOpsPerWave];            // tile row of this lane in op i
-    uint32_t kch[kOpsPerWave];          // byte offset of this lane's K chunk in op i
-#pragma unroll
-    for (int i = 0; i < kOpsPerWave; ++i) {
-        r_lane[i] = (wave * kOpsPerWave + i) * kRowsPerOp + lane_row;
-        kch[i] = (uint32_t)((lane_pc ^ swz_k(r_lane[i])) & (kCH - 1)) << 4;
-    }
-    // V chunk: op rows start at multiples of 4, so row & 3 == lane_row & 3
+    const uint32_t r_lane0 = (uint32_t)(wave * kOpsPerWave * kRowsPerOp + lane_row);   // tile row in op 0
+    const uint32_t kch = (uint32_t)k_pos<D>(lane_pc, lane_row) << 4;
     const uint32_t vch = (uint32_t)v_chunk_at<D>(lane_pc, lane_row) << 4;
 
-    u32x4_t rsk = {0u, 0u, 0u, 0x00020000u};   // K and V resources of the current full tile
-    u32x4_t rsv = rsk;
+    uint64_t kbase = 0, vbase = 0;            // K and V tile bases of the current full tile (less the bias)
+    uint32_t nrec = 0;                        // records in range (0: the empty look-ahead)
     uint32_t step_k = 0, step_v = 0;          // 64 rows of the current tensor, bytes
-    uint32_t koff[kOpsPerWave], voff[kOpsPerWave];
-#pragma unroll
-    for (int i = 0; i < kOpsPerWave; ++i) koff[i] = voff[i] = 0;
-    auto uniform_rsrc = [&](u32x4_t r) __attribute__((always_inline)) {
-        return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane(r[0]), (uint32_t)__builtin_amdgcn_readfirstlane(r[1]),
-                       (uint32_t)__builtin_amdgcn_readfirstlane(r[2]), 0x00020000u};
-    };
+    uint32_t kblk = 0, vblk = 0;              // kRowsPerOp rows of the current tensor less kBlockBytes
+    uint32_t koff = 0, voff = 0;
     // Point the copy state at full tile t (npart <= t < ntiles).
     auto set_full_tile = [&](int t) __attribute__((always_inline)) {
         const bool suf = t >= npart + Pf;
@@ -484,36 +519,35 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         const uintptr_t vb_s = reinterpret_cast<uintptr_t>(vs) + 2 * tsf * vs_ts;
         const uint32_t ksb = 2u * (uint32_t)(suf ? ks_ts : kp_ts);
         const uint32_t vsb = 2u * (uint32_t)(suf ? vs_ts : vp_ts);
-        rsk = uniform_rsrc(make_rsrc(suf ? kb_s : kb_p, ~0u));
-        rsv = uniform_rsrc(make_rsrc(suf ? vb_s : vb_p, ~0u));
+        kbase = uniform64((suf ? kb_s : kb_p) - kCopyBias);
+        vbase = uniform64((suf ? vb_s : vb_p) - kCopyBias);
+        nrec = ~0u;
         step_k = __builtin_amdgcn_readfirstlane(ksb * (uint32_t)kBN);
         step_v = __builtin_amdgcn_readfirstlane(vsb * (uint32_t)kBN);
-#pragma unroll
-        for (int i = 0; i < kOpsPerWave; ++i) {
-            koff[i] = __umul24((uint32_t)r_lane[i], ksb) + kch[i];
-            voff[i] = __umul24((uint32_t)r_lane[i], vsb) + vch;
-        }
+        kblk = __builtin_amdgcn_readfirstlane(ksb * (uint32_t)kRowsPerOp - (uint32_t)kBlockBytes);
+        vblk = __builtin_amdgcn_readfirstlane(vsb * (uint32_t)kRowsPerOp - (uint32_t)kBlockBytes);
+        koff = __umul24(r_lane0, ksb) + kch;
+        voff = __umul24(r_lane0, vsb) + vch;
     };
-    // Next full tile of the same tensor: base + 64 rows (the base stays below
-    // 2^48, so word 1 holds only address bits and no carry leaves it).
-    auto advance = [&](u32x4_t& r, uint32_t step) __attribute__((always_inline)) {
-        const uint64_t b = ((uint64_t)r[1] << 32 | r[0]) + step;
-        r = uniform_rsrc(u32x4_t{(uint32_t)b, (uint32_t)(b >> 32), r[2], 0x00020000u});
-    };
-    // Job J of the copy of the current full tile: even J = K of op J/2, odd = V.
-    // LDS byte address of this wave's rows in buffer 0 (K and V); a tile
-    // slot and an op add a compile-time offset.
+    // Job J of the copy of the current full tile: K of op J for J below
+    // kOpsPerWave, then V of op J - kOpsPerWave.  Each tensor's first op
+    // sets m0 to this wave's first block in the tile slot, the others reuse it.
     const uint32_t kdst0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(lds_k + wave * kOpsPerWave * kRowsPerOp * D));
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(lds_k + wave * kOpsPerWave * kBlockElems));
     const uint32_t vdst0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(lds_v + wave * kOpsPerWave * kRowsPerOp * D));
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(lds_v + wave * kOpsPerWave * kBlockElems));
+    uint32_t m0_copy = 0;
     auto fast_job = [&](auto SLOT, auto J) __attribute__((always_inline)) {
-        constexpr int i = decltype(J)::value / 2;
-        constexpr int off = (decltype(SLOT)::value * kTile + i * kRowsPerOp * D) * 2;
-        if constexpr (decltype(J)::value % 2 == 0)
-            lds_copy16_buf<off>(rsk, koff[i], kdst0);
+        constexpr int j = decltype(J)::value;
+        constexpr bool is_k = j < kOpsPerWave;
+        constexpr int i = is_k ? j : j - kOpsPerWave;
+        constexpr int slot_off = decltype(SLOT)::value * kTile * 2;
+        const u32x4_t rs = make_rsrc(is_k ? kbase : vbase, nrec);
+        const uint32_t soff = kCopyBias + (uint32_t)i * (is_k ? kblk : vblk);
+        if constexpr (i == 0)
+            m0_copy = lds_copy16_buf_m0<slot_off>(rs, is_k ? koff : voff, soff, is_k ? kdst0 : vdst0);
         else
-            lds_copy16_buf<off>(rsv, voff[i], vdst0);
+            lds_copy16_buf_at<i * kBlockBytes>(rs, is_k ? koff : voff, soff, m0_copy);
     };
     // Whole-tile copy issued at once (before the loop).
     auto dma_tile_now = [&](int t, auto SLOT) __attribute__((always_inline)) {
@@ -539,18 +573,18 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     int k_lane[kDS];
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds)
-        k_lane[ds] = krow * D + (((2 * ds + h) ^ swz_k(krow)) & (kCH - 1)) * 8;
+        k_lane[ds] = row_elems<D>(krow) + k_pos<D>(2 * ds + h, krow) * 8;
     const int tr_k = (lane & 15) >> 2;       // key offset supplied by this lane
     const int tr_q = lane & 3;               // 4-feature group supplied by this lane
     const int tr_half = (lane >> 4) & 1;     // which 16 features of the 32-block
     int v_lane[kDB];
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
-        v_lane[db] = (8 * h + tr_k) * D +
+        v_lane[db] = row_elems<D>(8 * h + tr_k) +
                      (2 * v_pos<D>(4 * db + 2 * tr_half + (tr_q >> 1), 8 * h + tr_k) + (tr_q & 1)) * 4;
 
     auto read_k = [&](auto SLOT, auto KB, int ds) __attribute__((always_inline)) {
-        constexpr int off = decltype(KB)::value * 32 * D;
+        constexpr int off = row_elems<D>(decltype(KB)::value * 32);
         return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(kbuf(SLOT) + k_lane[ds] + off));
     };
 
@@ -665,7 +699,9 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
     };
     auto read_v_half = [&](auto SLOT, auto KB, int f, int half) __attribute__((always_inline)) {
         const int db = f / 2, u = f % 2;
-        const uint16_t* a = vbuf(SLOT) + v_lane[db] + (decltype(KB)::value * 32 + 16 * u) * D + half * 4 * D;
+        // rows 8h + tr_k (in v_lane) plus 32 KB + 16 u + 4 half: the two
+        // parts never carry across a copy block, so their offsets add
+        const uint16_t* a = vbuf(SLOT) + v_lane[db] + row_elems<D>(decltype(KB)::value * 32 + 16 * u + 4 * half);
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a));
     };
     auto unit = [&](auto KSN, auto KBN, auto VS, auto KBC, auto KSNN, auto KBNN,
@@ -769,13 +805,12 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         // rows, or switch to the suffix, or an empty resource past the end.
         const int tt = t0 + r + 3;
         if (r + 3 >= nt) {
-            rsk[2] = 0u;
-            rsv[2] = 0u;
+            nrec = 0u;
         } else if (tt == npart + Pf) {
             set_full_tile(tt);
         } else {
-            advance(rsk, step_k);
-            advance(rsv, step_v);
+            kbase += step_k;
+            vbase += step_v;
         }
         auto copy_jobs = [&](auto J) __attribute__((always_inline)) { fast_job(ic<s3>{}, J); };
         auto no_jobs = [&](auto J) __attribute__((always_inline)) {};
