@@ -19,12 +19,15 @@
 //   consecutive keys: they become the bf16 B operand of O^T += V^T P^T with
 //   no data movement.
 // * K and V tiles are copied global -> LDS by direct-to-LDS loads (16 bytes
-//   per lane, no staging registers) into natural [key][d] tiles; the V^T
-//   operand is read with the gfx950 LDS transpose load ds_read_b64_tr_b16.
-//   XOR swizzles of the 16-byte chunks keep the reads free of bank conflicts.  Four K and four V tile buffers, each its own LDS
-//   array: tile t+3 is fetched while tile t is computed (its loads issued
-//   from the MFMA slots), and the per-tile barrier only waits for the copy
-//   issued one tile earlier.
+//   per lane, no staging registers) into [key][d] tiles laid out as 1 KB
+//   blocks of rows with a 16-byte pad after each block; the V^T operand is
+//   read with the gfx950 LDS transpose load ds_read_b64_tr_b16.  XOR
+//   swizzles of the 16-byte chunks keep the reads free of bank conflicts,
+//   and because the pad shifts each block by one bank group, a wave's
+//   copies of one tensor in one tile share one per-lane offset and one m0.
+//   Four K and four V tile buffers, each its own LDS array: tile t+3 is
+//   fetched while tile t is computed (its loads issued from the MFMA slots),
+//   and the per-tile barrier leaves only that newest copy in flight.
 // * Software pipeline inside each wave over 32-key units: the QK^T MFMAs of
 //   unit u+1 are issued alongside the weights of unit u (second query
 //   block), and the PV MFMAs of unit u alongside the first query block's
