@@ -707,6 +707,17 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
         const uint16_t* a = vbuf(SLOT) + v_lane[db] + row_elems<D>(decltype(KB)::value * 32 + 16 * u + 4 * half);
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(a));
     };
+    // End of an MFMA slot: its instructions issue as the MFMA, then its LDS
+    // read, then the VALU work (sched_group_barrier masks 0x8 MFMA, 0x100 LDS
+    // read, 0x2 VALU), and nothing crosses into the next slot.  Measured
+    // 0.5-1% faster than leaving the order within a slot to the scheduler,
+    // and 3-4% faster than putting the LDS read first.
+    auto slot_end = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
     auto unit = [&](auto KSN, auto KBN, auto VS, auto KBC, auto KSNN, auto KBNN,
                     f32x16_t (&sc)[kQB], f32x16_t (&sn)[kQB], const bf16x8_t (&pc0)[2],
                     bf16x8_t (&pn0)[2], bool valid_next, auto MASK_NEXT, auto&& jobs) __attribute__((always_inline)) {
@@ -728,7 +739,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
             });
             if constexpr (i % 2 == 0) vlo[i / 2] = read_v_half(VS, KBC, i / 2, 0);
             else vhi[i / 2] = read_v_half(VS, KBC, i / 2, 1);
-            __builtin_amdgcn_sched_barrier(0);
+            slot_end();
         });
         w_tail(w1);
         settle(ic<1>{}, sc[1], w1, true);
@@ -754,7 +765,7 @@ void jpa_fwd_kernel(const jpa_kernel_params p) {
             });
             if constexpr (i % 2 == 0) kq[i / 2] = read_k(KSNN, KBNN, i / 2);
             else jobs(ic<i / 2>{});                  // next-tile copy (first unit of a tile)
-            __builtin_amdgcn_sched_barrier(0);
+            slot_end();
         });
         w_tail(w0);
         settle(ic<0>{}, sn[0], w0, valid_next);
