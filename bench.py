@@ -192,6 +192,14 @@ def host_facts():
             "cpu_model": cpu_model()}
 
 
+def figure(x: float, decimals: int = 2) -> float:
+    """A reported figure: `decimals` places, or four significant digits when
+    that would round a small positive value (the launch-bound workload's
+    TFLOP/s) to nothing."""
+    r = round(x, decimals)
+    return r if abs(r) >= 10 ** (2 - decimals) or x == 0 else float(f"{x:.4g}")
+
+
 def _read(path):
     try:
         with open(path) as f:
@@ -586,7 +594,7 @@ def main():
 
     result = {
         "metric": METRIC,
-        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "value": figure(flops / (ms_per_step * 1e-3) / 1e12),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -604,8 +612,8 @@ def main():
                    "valid_flops": flops, **({"rank_share": share} if share else {}),
                    **({"split_wgs": args.split_wgs} if args.split_wgs else {})},
         "pct_of_bf16_peak": round(100.0 * flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": figure(achieved), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": figure(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": KERNEL_NAME,
                      "kernel_ms": {"mean": round(kern_ms, 4),
                                    "per_launch_pass": {"median": round(float(np.median(per_launch_ms)), 4),

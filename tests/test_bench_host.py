@@ -61,3 +61,15 @@ def test_git_head_follows_a_symbolic_ref(tmp_path, monkeypatch):
     assert bench._git_head() == "fedc" * 10
     monkeypatch.setattr(bench.os.path, "abspath", lambda p: str(tmp_path / "sub" / "bench.py"))
     assert bench._git_head() is None
+
+
+def test_reported_figures_keep_small_values():
+    """Throughputs are reported to two decimals, but a launch-bound workload's
+    TFLOP/s (well below 0.01) keeps four significant digits instead of
+    rounding to zero."""
+    assert bench.figure(1298.6612) == 1298.66
+    assert bench.figure(0.52) == 0.52
+    assert bench.figure(0.0078123) == 0.007812
+    assert bench.figure(0.0) == 0.0
+    assert bench.figure(1298.6612 / 2500, 4) == 0.5195
+    assert bench.figure(0.0078123 / 2500, 4) == 3.125e-06
